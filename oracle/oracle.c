@@ -1,0 +1,354 @@
+/*
+ * CPU oracle for the fused Indexer-TopK and the standalone ragged Top-k.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  It shares no code, header, table
+ * or constant with the HIP library: the formats are decoded here from their
+ * published definitions, the score is the plain sum, and selection is a full
+ * sort.  Nothing here is blocked, fused or reordered.
+ *
+ * What it computes (the plain definitions):
+ *
+ *  - Lightning-indexer score (LiteTopK, Sec. 2.1, Eq. (1)):
+ *        I[t,j] = sum_h w[t,h] * ReLU( q[t,h,:] . k[j,:] )
+ *    over the causally valid keys j < kv_len[t].  Weights are per query
+ *    (Eq. (1) indexes them by t).  With the NO_RELU flag and H = 1 the score
+ *    is the plain inner product q[t,0,:] . k[j,:] (the k-NN case of the
+ *    problem definition, LiteTopK Sec. 3.1 Eq. (2)).
+ *    FP8 keys are dequantised as decode(k8[j,d]) * scale[j].
+ *    Arithmetic: every input is widened exactly to double; products and sums
+ *    are accumulated in double, sequentially over d and then over h.
+ *
+ *  - Exact Top-k (LiteTopK Sec. 3.1 Eq. (2); the exactness criterion of the
+ *    Sample-Guided Exact Top-K paper, Sec. 6.1 Eq. (30)): sort the valid
+ *    entries of a row by (score descending, index ascending) and keep the
+ *    first min(k, L).  Equal scores (including -0 == +0) go to the lower
+ *    index.  Output slots past min(k, L) hold index -1.
+ *
+ * Formats (decoded from their definitions, not by bit reinterpretation):
+ *  - bf16: 1 sign, 8 exponent (bias 127), 7 fraction bits.
+ *  - fp16 (IEEE-754 binary16): 1 sign, 5 exponent (bias 15), 10 fraction bits.
+ *  - e4m3fn (OCP 8-bit floating point, E4M3): 1 sign, 4 exponent (bias 7),
+ *    3 fraction bits, no infinities, S.1111.111 is NaN, largest finite 448.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_F16 = 2, ORA_FP8_E4M3 = 3 };
+enum { ORA_FLAG_NO_RELU = 1 };
+
+/* Generic binary floating-point decode: sign bit, ebits exponent bits,
+ * mbits fraction bits, bias; `has_inf` selects IEEE-style inf/NaN at the top
+ * exponent, otherwise only the all-ones code is NaN (e4m3fn). */
+static double decode_generic(uint32_t bits, int ebits, int mbits, int bias, int has_inf)
+{
+    uint32_t sign = (bits >> (ebits + mbits)) & 1u;
+    uint32_t e = (bits >> mbits) & ((1u << ebits) - 1u);
+    uint32_t m = bits & ((1u << mbits) - 1u);
+    uint32_t emax = (1u << ebits) - 1u;
+    double v;
+    if (has_inf && e == emax) {
+        v = (m == 0) ? INFINITY : NAN;
+    } else if (!has_inf && e == emax && m == (1u << mbits) - 1u) {
+        v = NAN;
+    } else if (e == 0) {
+        v = ldexp((double)m / (double)(1u << mbits), 1 - bias);
+    } else {
+        v = ldexp(1.0 + (double)m / (double)(1u << mbits), (int)e - bias);
+    }
+    return sign ? -v : v;
+}
+
+double ora_decode(int dtype, uint32_t bits)
+{
+    switch (dtype) {
+    case ORA_BF16: return decode_generic(bits & 0xFFFFu, 8, 7, 127, 1);
+    case ORA_F16: return decode_generic(bits & 0xFFFFu, 5, 10, 15, 1);
+    case ORA_FP8_E4M3: return decode_generic(bits & 0xFFu, 4, 3, 7, 0);
+    case ORA_F32: {
+        float f;
+        memcpy(&f, &bits, 4);
+        return (double)f;
+    }
+    default: return NAN;
+    }
+}
+
+void ora_decode_array(int dtype, const void *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t b = 0;
+        if (dtype == ORA_F32) b = ((const uint32_t *)src)[i];
+        else if (dtype == ORA_FP8_E4M3) b = ((const uint8_t *)src)[i];
+        else b = ((const uint16_t *)src)[i];
+        dst[i] = ora_decode(dtype, b);
+    }
+}
+
+/* ---- decode tables (built once from ora_decode) --------------------------- */
+static double g_lut16[3][65536];
+static double g_lut8[256];
+static pthread_once_t g_lut_once = PTHREAD_ONCE_INIT;
+static void build_luts(void)
+{
+    for (uint32_t b = 0; b < 65536u; ++b) {
+        g_lut16[ORA_BF16][b] = ora_decode(ORA_BF16, b);
+        g_lut16[ORA_F16][b] = ora_decode(ORA_F16, b);
+    }
+    for (uint32_t b = 0; b < 256u; ++b) g_lut8[b] = ora_decode(ORA_FP8_E4M3, b);
+}
+
+static inline double elem(const void *base, int dtype, int64_t i)
+{
+    if (dtype == ORA_F32) return (double)((const float *)base)[i];
+    if (dtype == ORA_FP8_E4M3) return g_lut8[((const uint8_t *)base)[i]];
+    return g_lut16[dtype][((const uint16_t *)base)[i]];
+}
+
+typedef struct {
+    const void *Q; int q_t;
+    const void *K; int k_t;
+    const float *k_scale;
+    const float *W;
+    int H, D;
+    uint32_t flags;
+} fused_args;
+
+/* Query rows widened once: qbuf[h*D + d] = q[t,h,d]. */
+static void load_query(const fused_args *a, int t, double *qbuf)
+{
+    for (int h = 0; h < a->H; ++h)
+        for (int d = 0; d < a->D; ++d)
+            qbuf[h * a->D + d] = elem(a->Q, a->q_t, ((int64_t)t * a->H + h) * a->D + d);
+}
+
+/* I[t,j]: the definition, in double (sequential over d, then over h). */
+static double score_key(const fused_args *a, const double *qbuf, int t, int64_t j, double *kbuf)
+{
+    const int H = a->H, D = a->D;
+    const double sc = (a->k_t == ORA_FP8_E4M3 && a->k_scale) ? (double)a->k_scale[j] : 1.0;
+    for (int d = 0; d < D; ++d) kbuf[d] = elem(a->K, a->k_t, j * D + d) * sc;
+    double s = 0.0;
+    for (int h = 0; h < H; ++h) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qbuf[h * D + d] * kbuf[d];
+        const double w = (double)a->W[(int64_t)t * H + h];
+        if (a->flags & ORA_FLAG_NO_RELU) s += w * dot;
+        else s += w * (dot > 0.0 ? dot : 0.0);
+    }
+    return s;
+}
+
+/* Full score row of query t over keys [0, L). */
+static void score_row(const fused_args *a, int t, int64_t L, double *out, double *qbuf, double *kbuf)
+{
+    load_query(a, t, qbuf);
+    for (int64_t j = 0; j < L; ++j) out[j] = score_key(a, qbuf, t, j, kbuf);
+}
+
+/* ---- selection: full sort by (value desc, index asc) ----------------------- */
+typedef struct { double v; int64_t i; } vi_t;
+
+static int cmp_vi(const void *pa, const void *pb)
+{
+    const vi_t *a = (const vi_t *)pa, *b = (const vi_t *)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->i < b->i) ? -1 : (a->i > b->i);
+}
+
+/* Returns min(k, L); writes indices of the top min(k, L) in sorted order,
+ * pads the rest of out_idx[0..k) with -1, and (optionally) their scores. */
+static int select_sorted(vi_t *buf, int64_t L, int k, int32_t *out_idx, double *out_val)
+{
+    qsort(buf, (size_t)L, sizeof(vi_t), cmp_vi);
+    int n = (L < k) ? (int)L : k;
+    for (int r = 0; r < k; ++r) {
+        if (r < n) {
+            out_idx[r] = (int32_t)buf[r].i;
+            if (out_val) out_val[r] = buf[r].v;
+        } else {
+            out_idx[r] = -1;
+            if (out_val) out_val[r] = -INFINITY;
+        }
+    }
+    return n;
+}
+
+int ora_select_f64(const double *s, int64_t L, int k, int32_t *out_idx, double *out_val)
+{
+    if (L < 0 || k <= 0) return -1;
+    vi_t *buf = (vi_t *)malloc(sizeof(vi_t) * (size_t)(L > 0 ? L : 1));
+    if (!buf) return -2;
+    for (int64_t j = 0; j < L; ++j) { buf[j].v = s[j]; buf[j].i = j; }
+    int n = select_sorted(buf, L, k, out_idx, out_val);
+    free(buf);
+    return n;
+}
+
+int ora_select_f32(const float *s, int64_t L, int k, int32_t *out_idx)
+{
+    if (L < 0 || k <= 0) return -1;
+    vi_t *buf = (vi_t *)malloc(sizeof(vi_t) * (size_t)(L > 0 ? L : 1));
+    if (!buf) return -2;
+    for (int64_t j = 0; j < L; ++j) { buf[j].v = (double)s[j]; buf[j].i = j; }
+    int n = select_sorted(buf, L, k, out_idx, NULL);
+    free(buf);
+    return n;
+}
+
+/* ---- threaded drivers: one worker per core, rows handed out in order ------ */
+typedef struct {
+    /* fused */
+    fused_args fa;
+    const int32_t *kv_len;
+    /* ragged */
+    const float *scores;
+    int64_t pitch;
+    const int32_t *row_len;
+    /* common */
+    const int32_t *rows;
+    int nrows, k;
+    int32_t *out_idx;
+    double *out_val;
+    int32_t *out_n;
+    int64_t maxL;
+    int next;
+    int status;
+    pthread_mutex_t mu;
+} job_t;
+
+static int take_row(job_t *j)
+{
+    pthread_mutex_lock(&j->mu);
+    int r = j->next < j->nrows ? j->next++ : -1;
+    pthread_mutex_unlock(&j->mu);
+    return r;
+}
+
+static void *fused_worker(void *p)
+{
+    job_t *j = (job_t *)p;
+    const int H = j->fa.H, D = j->fa.D;
+    double *qbuf = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *kbuf = (double *)malloc(sizeof(double) * (size_t)D);
+    double *row = (double *)malloc(sizeof(double) * (size_t)(j->maxL > 0 ? j->maxL : 1));
+    vi_t *buf = (vi_t *)malloc(sizeof(vi_t) * (size_t)(j->maxL > 0 ? j->maxL : 1));
+    if (!qbuf || !kbuf || !row || !buf) { j->status = -2; goto out; }
+    for (int r; (r = take_row(j)) >= 0;) {
+        int t = j->rows[r];
+        int64_t L = j->kv_len[t];
+        score_row(&j->fa, t, L, row, qbuf, kbuf);
+        for (int64_t x = 0; x < L; ++x) { buf[x].v = row[x]; buf[x].i = x; }
+        j->out_n[r] = select_sorted(buf, L, j->k, j->out_idx + (int64_t)r * j->k,
+                                    j->out_val ? j->out_val + (int64_t)r * j->k : NULL);
+    }
+out:
+    free(qbuf); free(kbuf); free(row); free(buf);
+    return NULL;
+}
+
+static void *ragged_worker(void *p)
+{
+    job_t *j = (job_t *)p;
+    vi_t *buf = (vi_t *)malloc(sizeof(vi_t) * (size_t)(j->maxL > 0 ? j->maxL : 1));
+    if (!buf) { j->status = -2; return NULL; }
+    for (int r; (r = take_row(j)) >= 0;) {
+        int m = j->rows[r];
+        int64_t L = j->row_len[m];
+        if (L > j->pitch) L = j->pitch;
+        if (L < 0) L = 0;
+        const float *x = j->scores + (int64_t)m * j->pitch;
+        for (int64_t i = 0; i < L; ++i) { buf[i].v = (double)x[i]; buf[i].i = i; }
+        j->out_n[r] = select_sorted(buf, L, j->k, j->out_idx + (int64_t)r * j->k, NULL);
+    }
+    free(buf);
+    return NULL;
+}
+
+static int run_threads(job_t *j, void *(*fn)(void *), int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    pthread_mutex_init(&j->mu, NULL);
+    j->next = 0;
+    j->status = 0;
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i)
+        if (pthread_create(&th[i], NULL, fn, j) == 0) ++started;
+    if (started == 0) fn(j);
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    pthread_mutex_destroy(&j->mu);
+    return j->status;
+}
+
+/* Top-k of the fused score for the listed query rows.
+ * out_idx/out_val: [nrows, k]; out_n: [nrows] = min(k, kv_len[t]). */
+int ora_fused_topk(const void *Q, int q_t, const void *K, int k_t, const float *k_scale,
+                   const float *W, const int32_t *kv_len, int H, int D, uint32_t flags,
+                   const int32_t *rows, int nrows, int k, int32_t *out_idx, double *out_val,
+                   int32_t *out_n, int nthreads)
+{
+    pthread_once(&g_lut_once, build_luts);
+    if (k <= 0 || H <= 0 || D <= 0 || nrows < 0) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.fa = (fused_args){Q, q_t, K, k_t, k_scale, W, H, D, flags};
+    j.kv_len = kv_len;
+    j.rows = rows; j.nrows = nrows; j.k = k;
+    j.out_idx = out_idx; j.out_val = out_val; j.out_n = out_n;
+    for (int r = 0; r < nrows; ++r)
+        if (kv_len[rows[r]] > j.maxL) j.maxL = kv_len[rows[r]];
+    return run_threads(&j, fused_worker, nthreads);
+}
+
+/* Score of single (query, key) pairs: out[i] = I[t[i], j[i]]. */
+int ora_fused_scores_at(const void *Q, int q_t, const void *K, int k_t, const float *k_scale,
+                        const float *W, int H, int D, uint32_t flags, const int32_t *t_idx,
+                        const int64_t *j_idx, int64_t n, double *out)
+{
+    pthread_once(&g_lut_once, build_luts);
+    fused_args a = {Q, q_t, K, k_t, k_scale, W, H, D, flags};
+    double *qbuf = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *kbuf = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!qbuf || !kbuf) { free(qbuf); free(kbuf); return -2; }
+    for (int64_t i = 0; i < n; ++i) {
+        load_query(&a, t_idx[i], qbuf);
+        out[i] = score_key(&a, qbuf, t_idx[i], j_idx[i], kbuf);
+    }
+    free(qbuf); free(kbuf);
+    return 0;
+}
+
+/* Full score row of query t over keys [0, L). */
+int ora_fused_score_row(const void *Q, int q_t, const void *K, int k_t, const float *k_scale,
+                        const float *W, int H, int D, uint32_t flags, int t, int64_t L, double *out)
+{
+    pthread_once(&g_lut_once, build_luts);
+    fused_args a = {Q, q_t, K, k_t, k_scale, W, H, D, flags};
+    double *qbuf = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *kbuf = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!qbuf || !kbuf) { free(qbuf); free(kbuf); return -2; }
+    score_row(&a, t, L, out, qbuf, kbuf);
+    free(qbuf); free(kbuf);
+    return 0;
+}
+
+/* Standalone exact Top-k of the listed rows of a [M, pitch] fp32 matrix. */
+int ora_topk_ragged(const float *scores, int64_t pitch, const int32_t *row_len,
+                    const int32_t *rows, int nrows, int k, int32_t *out_idx, int32_t *out_n,
+                    int nthreads)
+{
+    if (k <= 0 || pitch < 0 || nrows < 0) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.scores = scores; j.pitch = pitch; j.row_len = row_len;
+    j.rows = rows; j.nrows = nrows; j.k = k;
+    j.out_idx = out_idx; j.out_n = out_n;
+    j.maxL = pitch;
+    return run_threads(&j, ragged_worker, nthreads);
+}

@@ -1,0 +1,251 @@
+"""Pins for the CPU oracle (runs without a GPU).
+
+Each test ties the oracle to something other than itself, chosen so that a
+plausible mistake (a dropped head or dimension, a wrong sign in the ReLU, a
+transposed operand, per-head instead of per-query weights, a wrong tie rule,
+ignoring the causal length) fails at least one of them:
+
+* exhaustive decode of every bf16 / fp16 / e4m3fn code against torch/numpy;
+* H = 1 without ReLU against numpy's matmul (LiteTopK Sec. 3.1, k-NN case);
+* the ReLU score on the positive orthant, where ReLU is the identity and the
+  score collapses to a weighted matmul (LiteTopK Sec. 2.1 Eq. (1));
+* heads whose query is negated on the positive orthant contribute nothing;
+* positive homogeneity of the ReLU score in the per-key FP8 scale;
+* a monotone closed form whose Top-k is the last k valid keys;
+* selection against brute-force enumeration of all subsets on tiny rows, the
+  exactness criterion (Sample-Guided Exact Top-K Sec. 6.1 Eq. (30)) and
+  numpy's lexsort.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+# ----------------------------------------------------------------- decoders
+@pytest.mark.parametrize("dtype,nbits", [(synth.BF16, 16), (synth.F16, 16), (synth.FP8_E4M3, 8)])
+def test_decode_exhaustive_against_library_casts(dtype, nbits):
+    codes = np.arange(1 << nbits, dtype=np.uint16 if nbits == 16 else np.uint8)
+    ours = oracle.decode(codes, dtype)
+    ref = synth.decode_reference_free(codes, dtype).astype(np.float64)
+    nan_ours, nan_ref = np.isnan(ours), np.isnan(ref)
+    assert np.array_equal(nan_ours, nan_ref)
+    assert np.array_equal(ours[~nan_ours], ref[~nan_ref])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(ours[~nan_ours]), np.signbit(ref[~nan_ref]))
+
+
+def test_decode_e4m3fn_landmarks():
+    # OCP E4M3: 0x7E = 448 (largest finite), 0x08 = 2^-6 (smallest normal),
+    # 0x01 = 2^-9 (smallest subnormal), 0x7F and 0xFF are NaN, 0x38 = 1.0.
+    v = oracle.decode(np.array([0x7E, 0x08, 0x01, 0x38, 0xB8], dtype=np.uint8), synth.FP8_E4M3)
+    assert list(v) == [448.0, 2.0 ** -6, 2.0 ** -9, 1.0, -1.0]
+    assert np.isnan(oracle.decode(np.array([0x7F, 0xFF], dtype=np.uint8), synth.FP8_E4M3)).all()
+
+
+def _case(T, H, D, N, k, *, q=None, kk=None, W=None, kv_len=None, q_dtype=synth.F32,
+          k_dtype=synth.F32, k_scale=None, no_relu=False):
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((T, H, D)).astype(np.float32) if q is None else q.astype(np.float32)
+    kk = rng.standard_normal((N, D)).astype(np.float32) if kk is None else kk.astype(np.float32)
+    W = rng.random((T, H)).astype(np.float32) if W is None else W.astype(np.float32)
+    kvl = np.full(T, N, np.int32) if kv_len is None else np.asarray(kv_len, np.int32)
+    return synth.FusedCase(name="pin", T=T, H=H, D=D, N=N, k=k, q_dtype=q_dtype, k_dtype=k_dtype,
+                           q_bits=synth.encode(q, q_dtype), k_bits=synth.encode(kk, k_dtype),
+                           k_scale=k_scale, W=W, kv_len=kvl,
+                           flags=synth.FLAG_NO_RELU if no_relu else 0)
+
+
+def _all_rows(case):
+    return np.stack([oracle.fused_score_row(case, t, case.N) for t in range(case.T)])
+
+
+# ------------------------------------------------------------ score pins
+def test_inner_product_equals_numpy_matmul():
+    c = _case(5, 1, 24, 37, 4, W=np.ones((5, 1)), no_relu=True)
+    q = c.q_bits.reshape(5, 24).astype(np.float64)
+    ref = q @ c.k_bits.astype(np.float64).T
+    np.testing.assert_allclose(_all_rows(c), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_relu_score_on_positive_orthant_is_weighted_matmul():
+    rng = np.random.default_rng(1)
+    T, H, D, N = 4, 3, 8, 29
+    q = np.abs(rng.standard_normal((T, H, D)))
+    kk = np.abs(rng.standard_normal((N, D)))
+    W = rng.random((T, H))
+    c = _case(T, H, D, N, 3, q=q, kk=kk, W=W)
+    qf, kf, wf = (c.q_bits.astype(np.float64), c.k_bits.astype(np.float64), c.W.astype(np.float64))
+    # sum_h w[t,h] q[t,h,:] . k[j,:]  ==  (sum_h w[t,h] q[t,h,:]) @ K^T
+    ref = np.stack([(wf[t] @ qf[t]) @ kf.T for t in range(T)])
+    np.testing.assert_allclose(_all_rows(c), ref, rtol=1e-12)
+
+
+def test_negated_heads_contribute_nothing():
+    rng = np.random.default_rng(2)
+    T, H, D, N = 3, 4, 6, 17
+    q = np.abs(rng.standard_normal((T, H, D)))
+    q[:, 1] *= -1.0  # head 1 always scores <= 0 against positive keys
+    q[2, 3] *= -1.0  # and head 3 of query 2
+    kk = np.abs(rng.standard_normal((N, D)))
+    W = rng.random((T, H))
+    c = _case(T, H, D, N, 3, q=q, kk=kk, W=W)
+    qf, kf, wf = (c.q_bits.astype(np.float64), c.k_bits.astype(np.float64), c.W.astype(np.float64).copy())
+    wf[:, 1] = 0.0
+    wf[2, 3] = 0.0
+    ref = np.stack([(wf[t] @ qf[t]) @ kf.T for t in range(T)])
+    np.testing.assert_allclose(_all_rows(c), ref, rtol=1e-12, atol=1e-15)
+    # and the weights are per query: swapping two queries' weights changes rows
+    c2 = _case(T, H, D, N, 3, q=q, kk=kk, W=W[::-1].copy())
+    assert not np.allclose(_all_rows(c2)[0], _all_rows(c)[0])
+
+
+def test_fp8_per_key_scale_is_positively_homogeneous():
+    rng = np.random.default_rng(3)
+    T, H, D, N = 2, 3, 16, 21
+    kk = rng.standard_normal((N, D)).astype(np.float32)
+    ones = np.ones(N, np.float32)
+    scales = (2.0 ** rng.integers(-3, 4, size=N)).astype(np.float32)  # exact powers of two
+    base = _case(T, H, D, N, 4, kk=kk, k_dtype=synth.FP8_E4M3, k_scale=ones)
+    scaled = _case(T, H, D, N, 4, kk=kk, k_dtype=synth.FP8_E4M3, k_scale=scales)
+    np.testing.assert_allclose(_all_rows(scaled), _all_rows(base) * scales[None, :], rtol=1e-13)
+
+
+def test_monotone_keys_select_last_valid_keys():
+    # D = 1, q = 1, k_j = j/64: every score is (sum_h w) * j/64, increasing in j,
+    # so the Top-k of query t is the last k keys below kv_len[t].
+    T, H, N, k = 4, 2, 300, 16
+    q = np.ones((T, H, 1))
+    kk = (np.arange(N, dtype=np.float64) / 64.0)[:, None]
+    kv_len = np.array([300, 250, 16, 5])
+    c = _case(T, H, 1, N, k, q=q, kk=kk, kv_len=kv_len)
+    idx, val, n = oracle.fused_topk(c)
+    for t in range(T):
+        L = int(kv_len[t])
+        exp = list(range(L - 1, max(L - k, 0) - 1, -1))
+        assert n[t] == min(k, L)
+        assert list(idx[t, :n[t]]) == exp
+        assert (idx[t, n[t]:] == -1).all() and np.isneginf(val[t, n[t]:]).all()
+
+
+def test_all_relu_zero_rows_select_lowest_indices():
+    rng = np.random.default_rng(4)
+    T, H, D, N, k = 2, 3, 8, 50, 7
+    q = -np.abs(rng.standard_normal((T, H, D)))
+    kk = np.abs(rng.standard_normal((N, D)))
+    c = _case(T, H, D, N, k, q=q, kk=kk)
+    idx, val, n = oracle.fused_topk(c)
+    assert (val[:, :k] == 0.0).all()
+    assert (idx == np.arange(k)[None, :]).all()
+
+
+def test_fused_topk_matches_selection_of_score_row():
+    c = synth.gen_fused(6, 4, 16, 200, 9, q_dtype=synth.BF16, k_dtype=synth.BF16,
+                        kv_len=[200, 150, 9, 3, 1, 120], seed=11)
+    idx, val, n = oracle.fused_topk(c, nthreads=3)
+    sidx, sval, sn = oracle.fused_topk(c, rows=[3, 0], nthreads=1)
+    assert np.array_equal(sidx, idx[[3, 0]]) and np.array_equal(sval, val[[3, 0]])
+    for t in range(c.T):
+        row = oracle.fused_score_row(c, t)
+        order = np.lexsort((np.arange(row.size), -row))[: c.k]
+        assert n[t] == min(c.k, row.size)
+        assert list(idx[t, :n[t]]) == list(order)
+        pairs = oracle.fused_scores_at(c, np.full(n[t], t), idx[t, :n[t]])
+        assert np.array_equal(pairs, val[t, :n[t]])
+
+
+# -------------------------------------------------------- selection pins
+def _brute_force_topk_set(x, k):
+    """Enumerate every subset of size min(k, L); keep those that beat every
+    outsider under (value desc, index asc).  Exactly one must survive."""
+    L = len(x)
+    m = min(k, L)
+    winners = []
+    for S in itertools.combinations(range(L), m):
+        inside = set(S)
+        ok = all((x[i] > x[j]) or (x[i] == x[j] and i < j)
+                 for i in inside for j in range(L) if j not in inside)
+        if ok:
+            winners.append(inside)
+    assert len(winners) == 1
+    return winners[0]
+
+
+def test_selection_against_subset_enumeration():
+    rng = np.random.default_rng(5)
+    pool = np.array([-1.5, -0.0, 0.0, 0.25, 0.25, 3.0, np.inf, -np.inf], dtype=np.float32)
+    for trial in range(300):
+        L = int(rng.integers(0, 9))
+        k = int(rng.integers(1, 5))
+        x = rng.choice(pool, size=L).astype(np.float32)
+        idx, n = oracle.select(x, k)
+        assert n == min(k, L)
+        assert set(idx[:n].tolist()) == _brute_force_topk_set(x.tolist(), k)
+        assert (idx[n:] == -1).all()
+
+
+def test_selection_order_against_repeated_argmax():
+    rng = np.random.default_rng(6)
+    for trial in range(100):
+        L = int(rng.integers(1, 40))
+        k = int(rng.integers(1, 12))
+        x = rng.integers(-3, 4, size=L).astype(np.float32)
+        idx, n = oracle.select(x, k)
+        taken = np.zeros(L, bool)
+        for r in range(n):
+            best = -1
+            for j in range(L):  # first maximum among the untaken = lowest index
+                if not taken[j] and (best < 0 or x[j] > x[best]):
+                    best = j
+            taken[best] = True
+            assert idx[r] == best
+
+
+@pytest.mark.parametrize("family", synth.RAGGED_FAMILIES)
+def test_ragged_exactness_invariants(family):
+    c = synth.gen_ragged(6, 4096, 300, lens=[4096, 3000, 300, 299, 1, 0], seed=9, family=family)
+    idx, n = oracle.topk_ragged(c)
+    for r in range(c.M):
+        L = int(c.row_len[r])
+        x = c.scores[r, :L].astype(np.float64)
+        sel = idx[r, :n[r]]
+        assert n[r] == min(c.k, L)
+        assert len(set(sel.tolist())) == n[r]
+        assert ((sel >= 0) & (sel < L)).all() and (idx[r, n[r]:] == -1).all()
+        if 0 < n[r] < L:
+            # Eq. (30): min over selected >= max over the rest
+            mask = np.ones(L, bool)
+            mask[sel] = False
+            assert x[sel].min() >= x[mask].max()
+            # ties at the boundary go to the lowest indices
+            kth = x[sel].min()
+            eq = np.flatnonzero(x == kth)
+            n_above = int((x > kth).sum())
+            assert set(sel[x[sel] == kth].tolist()) == set(eq[: n[r] - n_above].tolist())
+        order = np.lexsort((np.arange(L), -x))[: c.k]
+        assert list(sel) == list(order)
+
+
+def test_ragged_ignores_padded_tail_and_signed_zero_ties():
+    scores = np.full((2, 8), np.inf, np.float32)  # +inf beyond row_len must be ignored
+    scores[0, :5] = [-0.0, 0.0, -0.0, -1.0, 0.0]
+    scores[1, :3] = [1.0, 2.0, 3.0]
+    c = synth.RaggedCase(name="z", M=2, pitch=8, k=2, scores=scores, row_len=np.array([5, 3], np.int32))
+    idx, n = oracle.topk_ragged(c)
+    assert list(idx[0]) == [0, 1]  # -0 == +0: lowest indices win
+    assert list(idx[1]) == [2, 1]
+
+
+def test_special_rows():
+    L, k = 1000, 64
+    idx, n = oracle.select(np.full(L, 0.5, np.float32), k)
+    assert list(idx) == list(range(k))
+    idx, n = oracle.select(np.arange(L, dtype=np.float32), k)
+    assert list(idx) == list(range(L - 1, L - 1 - k, -1))
+    idx, n = oracle.select(np.arange(10, dtype=np.float32), k)
+    assert n == 10 and list(idx[:10]) == list(range(9, -1, -1)) and (idx[10:] == -1).all()
+    idx, n = oracle.select(np.zeros(0, np.float32), k)
+    assert n == 0 and (idx == -1).all()

@@ -1,0 +1,49 @@
+"""The seeded generators are deterministic and draw the stated shapes/statistics."""
+import numpy as np
+
+import synth
+
+
+def test_fused_generator_is_deterministic_and_shaped():
+    a = synth.gen_fused(8, 4, 32, 100, 5, q_dtype=synth.BF16, k_dtype=synth.FP8_E4M3, seed=3)
+    b = synth.gen_fused(8, 4, 32, 100, 5, q_dtype=synth.BF16, k_dtype=synth.FP8_E4M3, seed=3)
+    c = synth.gen_fused(8, 4, 32, 100, 5, q_dtype=synth.BF16, k_dtype=synth.FP8_E4M3, seed=4)
+    assert np.array_equal(a.q_bits, b.q_bits) and np.array_equal(a.k_bits, b.k_bits)
+    assert not np.array_equal(a.q_bits, c.q_bits)
+    assert a.q_bits.shape == (8, 4, 32) and a.q_bits.dtype == np.uint16
+    assert a.k_bits.shape == (100, 32) and a.k_bits.dtype == np.uint8
+    assert a.k_scale.shape == (100,) and (a.k_scale > 0).all()
+    # every key row uses the full e4m3fn range: its largest magnitude code is 448
+    kd = np.abs(synth.decode_reference_free(a.k_bits, synth.FP8_E4M3))
+    assert np.allclose(kd.max(axis=1), 448.0)
+    assert (a.W >= 0).all() and (a.W <= 1.0 / 4).all()
+
+
+def test_config1_shapes_and_causal_lengths():
+    c = synth.fused_config(1)
+    assert (c.T, c.H, c.D, c.N, c.k) == (64, 8, 64, 4096, 256)
+    assert c.kv_len[0] == 4096 - 63 and c.kv_len[-1] == 4096
+    q = c.q_bits
+    assert abs(float(q.std()) - 1 / 8) < 0.01  # N(0,1)/sqrt(64)
+
+
+def test_config2_recipe():
+    c = synth.ragged_config()
+    assert (c.M, c.pitch, c.k) == (64, 131072, 2048)
+    assert c.row_len.min() >= 8192 and c.row_len.max() <= 131072
+    for r in range(4):
+        L = int(c.row_len[r])
+        x = c.scores[r, :L]
+        assert np.isneginf(c.scores[r, L:]).all()
+        assert np.isfinite(x).all()
+        # ~0.1% long tail around 4 and ~1% forced duplicates
+        assert 0.0004 * L < (x > 2.5).sum() < 0.004 * L
+        assert len(np.unique(x)) < L - 0.005 * L
+
+
+def test_unit_norm_embeddings():
+    c = synth.gen_fused(4, 1, 256, 64, 8, q_dtype=synth.F16, k_dtype=synth.F16, no_relu=True,
+                        unit_norm=True, seed=1)
+    k = synth.decode_reference_free(c.k_bits, synth.F16)
+    assert np.allclose(np.linalg.norm(k, axis=1), 1.0, atol=2e-3)
+    assert c.flags == synth.FLAG_NO_RELU and (c.W == 1).all()
