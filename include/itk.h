@@ -1,0 +1,176 @@
+/*
+ * itk.h — fused Indexer-TopK and exact ragged Top-k for AMD MI355X (gfx950).
+ *
+ * A small C ABI over hand-written HIP kernels.  Both operations are
+ * asynchronous on the caller's HIP stream: they validate their arguments on
+ * the host, enqueue a fixed sequence of kernels whose launch geometry depends
+ * only on the shape arguments, and return.  They never synchronize, never read
+ * device data back to the host and never allocate, so a call can be captured
+ * into a HIP graph and replayed.  The caller owns every buffer.
+ *
+ * Pointers are device pointers unless marked (host).  `stream` is a
+ * hipStream_t passed as void* (NULL = the default stream).
+ *
+ * Error behaviour: an invalid argument is reported synchronously by the status
+ * code and nothing is enqueued.  Conditions that depend on device data
+ * (too few or too many candidates after the sampled gate, ties, short rows)
+ * are never errors: they are resolved on the device by the exact recovery
+ * routes, so the result is always the exact Top-k.  Valid lengths larger than
+ * the row width are clamped to it; negative lengths are treated as 0.
+ */
+#ifndef ITK_H
+#define ITK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ITK_OK = 0,
+    ITK_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad dtype */
+    ITK_ERR_UNSUPPORTED = 2,   /* valid but not implemented shape or dtype pair */
+    ITK_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    ITK_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} itk_status;
+
+typedef enum {
+    ITK_F32 = 0,
+    ITK_BF16 = 1,
+    ITK_F16 = 2,
+    ITK_FP8_E4M3 = 3           /* OCP e4m3fn: 1-4-3, bias 7, max 448, no inf */
+} itk_dtype;
+
+/* Flag for indexer_topk_fused: plain inner-product score (k-NN retrieval,
+ * LiteTopK Sec. 3.1 Eq. (2)); requires H == 1; W[t,0] still multiplies. */
+#define ITK_FLAG_NO_RELU 1u
+
+/* ------------------------------------------------------------------------
+ * Standalone exact Top-k over materialized ragged fp32 rows.
+ *
+ * Operation (Sample-Guided Exact Top-K, arXiv 2609.08450, Sec. 2.1
+ * "Operator contract"; exactness criterion Sec. 6.1 Eq. (30)): for each row r
+ * with valid length L_r = clamp(row_len[r], 0, row_pitch), return the indices
+ * of the min(k, L_r) largest values of scores[r, 0:L_r].  Equal values
+ * (including -0 and +0) are resolved in favour of the lower index, so the
+ * returned set is unique.  NaN is a precondition violation.
+ *
+ *   scores   [M, row_pitch] fp32, row-major; only the first L_r entries of a
+ *            row are read.  row_pitch % 4 == 0 enables 16-byte loads.
+ *   row_len  [M] int32 (device), valid length of each row.
+ *   out_idx  [M, k] int32.  The first min(k, L_r) slots of row r hold the
+ *            selected indices in unspecified order; the rest hold -1.
+ *   workspace / workspace_bytes: scratch of at least
+ *            topk_ragged_workspace_size(M, row_pitch, k) bytes, 256-byte
+ *            aligned; contents need no initialisation and are meaningless
+ *            between calls.  Concurrent calls must not share a workspace.
+ *
+ * Method: a block-strided view of the row proposes a coarse boundary, one
+ * complete-row pass certifies it and collects the admitted candidates, and an
+ * exact radix refinement over (ordered fp32 key, inverted index) resolves the
+ * final set; underfilled views fall back to a band pass and then to an exact
+ * route that needs no sample (Sec. 4.2-4.4 of the same paper).
+ * ------------------------------------------------------------------------ */
+size_t topk_ragged_workspace_size(int32_t M, int64_t row_pitch, int32_t k);
+
+itk_status topk_ragged(const float *scores, int64_t row_pitch, const int32_t *row_len,
+                       int32_t M, int32_t k, int32_t *out_idx,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Fused lightning-indexer score + exact per-row Top-k.
+ *
+ * Operation (LiteTopK, arXiv 2607.11976, Sec. 2.1 Eq. (1) and Sec. 3.1
+ * Eq. (2)): for each query t and each causally valid key j < L_t with
+ * L_t = clamp(kv_len[t], 0, N),
+ *     s[t,j] = sum_h W[t,h] * ReLU( Q[t,h,:] . Khat[j,:] )
+ * (with ITK_FLAG_NO_RELU: s[t,j] = W[t,0] * Q[t,0,:] . Khat[j,:]), where
+ * Khat = K for bf16/fp16/fp32 keys and Khat[j,:] = decode(K[j,:]) * k_scale[j]
+ * for e4m3fn keys.  Return the min(k, L_t) keys of largest score, ties to the
+ * lower index, without materializing the [T, N] score matrix.
+ *
+ *   Q        [T, H, D] row-major, dtype q_t
+ *   K        [N, D] row-major, dtype k_t
+ *   k_scale  [N] fp32, required iff k_t == ITK_FP8_E4M3; entries must be
+ *            finite and >= 0 (the scale is applied after the ReLU, which is
+ *            exact only for non-negative scales).
+ *   W        [T, H] fp32 per-query head weights.
+ *   kv_len   [T] int32 (device).
+ *   out_idx  [T, k] int32: selected key indices in unspecified order, -1 pad.
+ *   out_score[T, k] fp32: the kernel's fp32 score of out_idx, -inf pad.
+ *   Supported (q_t, k_t): (BF16, BF16), (BF16, FP8_E4M3), (F16, F16),
+ *   (F16, FP8_E4M3), (F32, F32).  D in {64, 128, 256}; 1 <= H <= 64;
+ *   H > 32 needs D <= 128; F32 needs ceil(H/32) * D <= 128.
+ *   Scores are accumulated in fp32 (MFMA); selection is exact on those fp32
+ *   scores.  Scratch is O(T * k): see the workspace size query.
+ *   workspace: as for topk_ragged.
+ * ------------------------------------------------------------------------ */
+size_t indexer_topk_fused_workspace_size(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k,
+                                         itk_dtype q_t, itk_dtype k_t, uint32_t flags);
+
+itk_status indexer_topk_fused(const void *Q, itk_dtype q_t, const void *K, itk_dtype k_t,
+                              const float *k_scale, const float *W, const int32_t *kv_len,
+                              int32_t T, int32_t H, int32_t D, int64_t N, int32_t k,
+                              uint32_t flags, int32_t *out_idx, float *out_score,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *itk_status_string(itk_status status);
+
+/* ------------------------------------------------------------------------
+ * Test and measurement knobs (not needed for normal use).
+ * ------------------------------------------------------------------------ */
+
+/* Planner overrides.  A zero field keeps the default.  Process-global; they
+ * change efficiency, never results.  Workspace sizes depend on `capacity`,
+ * so query the size after setting the knobs. */
+typedef struct {
+    int32_t sample_stride;  /* ragged: view density 1/s (one 16-element block in s);
+                               fused: sampled tile stride (1 in N tiles of 64 keys) */
+    float rho;              /* primary target rank as a multiple of k */
+    float rho1;             /* ragged: secondary (band) target rank multiple */
+    int32_t capacity;       /* fused: candidates per row; ragged: per segment */
+    int32_t splits;         /* fused: key splits per query group;
+                               ragged: segments per row */
+    int32_t force_route;    /* 0 auto; 1 exact route for every row (ragged:
+                               no sample; fused: re-scoring recovery);
+                               2 ragged: force the band pass */
+} itk_plan_opts;
+
+/* NULL restores the defaults. */
+itk_status itk_set_plan_opts(const itk_plan_opts *opts);
+
+/* Route taken per row by the last calls: when `route_out` (device, [rows]
+ * int32) is non-NULL, each following call writes a route code per row:
+ *   1 certified by the sample, 2 certified after the band pass,
+ *   3 exact route (no usable sample, overflow, or underfill),
+ *   4 all valid entries fit the candidate capacity (no gate needed).
+ * Pass NULL to stop. */
+itk_status itk_set_route_buffer(int32_t *route_out, int32_t rows);
+
+/* Per-kernel timing.  While enabled, each call records HIP events around each
+ * kernel it launches; itk_profile_read sums the elapsed milliseconds per
+ * stage since the last read (synchronizing on the recorded events) and
+ * returns the number of stages written.  Stage names are static strings. */
+itk_status itk_profile_enable(int32_t on);
+int32_t itk_profile_read(double *ms_out, int32_t *count_out, const char **names_out, int32_t max_stages);
+
+/* Probes of the device building blocks, for tests only.
+ *  itk_debug_mfma: one 32x32 MFMA (mtype 0 bf16 x16, 1 fp16 x16, 2 fp32 x2);
+ *    lane l reads its A and B operand fragments from a_frags[l], b_frags[l]
+ *    (16 bytes each for bf16/fp16, 4 bytes for fp32) and writes its 16
+ *    accumulator values to c_out[16 l .. 16 l + 15].
+ *  itk_debug_fp8: widen n e4m3fn codes to bf16 and fp16 bit patterns.
+ *  itk_debug_coarse: the 11-bit coarse key of x[i] and the inclusive fp32
+ *    endpoint of coarse bin i, for i < n <= 2048. */
+itk_status itk_debug_mfma(int32_t mtype, const void *a_frags, const void *b_frags, float *c_out, void *stream);
+itk_status itk_debug_fp8(const uint8_t *in, uint16_t *bf16_out, uint16_t *f16_out, int32_t n, void *stream);
+itk_status itk_debug_coarse(const float *x, uint32_t *key_out, float *endpoint_out, int32_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ITK_H */

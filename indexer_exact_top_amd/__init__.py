@@ -1,0 +1,228 @@
+"""Python binding of the itk C ABI (include/itk.h): argument marshalling only.
+
+Every step of the fused Indexer-TopK and of the ragged Top-k runs in the HIP
+kernels of ``libitk.so``; this module only turns torch device tensors into
+pointers, allocates outputs and workspaces with torch (plumbing), and passes
+the current HIP stream.  There is no CPU fallback: the calls raise when the
+library or a GPU is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libitk.so")
+
+F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
+FLAG_NO_RELU = 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip error"}
+
+_lib = None
+
+
+class ITKError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({STATUS.get(status, '?')})")
+        self.status = status
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("sample_stride", ctypes.c_int32), ("rho", ctypes.c_float), ("rho1", ctypes.c_float),
+                ("capacity", ctypes.c_int32), ("splits", ctypes.c_int32), ("force_route", ctypes.c_int32)]
+
+
+def lib():
+    """Load libitk.so (built by ``build.py``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run indexer_exact_top_amd/build.py (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, U32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+        L.topk_ragged_workspace_size.argtypes = [I32, I64, I32]
+        L.topk_ragged_workspace_size.restype = SZ
+        L.topk_ragged.argtypes = [P, I64, P, I32, I32, P, P, SZ, P]
+        L.topk_ragged.restype = ctypes.c_int
+        L.indexer_topk_fused_workspace_size.argtypes = [I32, I32, I32, I64, I32, ctypes.c_int, ctypes.c_int, U32]
+        L.indexer_topk_fused_workspace_size.restype = SZ
+        L.indexer_topk_fused.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, P, P, I32, I32, I32, I64, I32, U32,
+                                         P, P, P, SZ, P]
+        L.indexer_topk_fused.restype = ctypes.c_int
+        L.itk_status_string.argtypes = [ctypes.c_int]
+        L.itk_status_string.restype = ctypes.c_char_p
+        L.itk_set_plan_opts.argtypes = [ctypes.POINTER(PlanOpts)]
+        L.itk_set_plan_opts.restype = ctypes.c_int
+        L.itk_set_route_buffer.argtypes = [P, I32]
+        L.itk_set_route_buffer.restype = ctypes.c_int
+        L.itk_profile_enable.argtypes = [I32]
+        L.itk_profile_enable.restype = ctypes.c_int
+        L.itk_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32),
+                                       ctypes.POINTER(ctypes.c_char_p), I32]
+        L.itk_profile_read.restype = I32
+        for name in ("itk_debug_mfma", "itk_debug_fp8", "itk_debug_coarse"):
+            getattr(L, name).restype = ctypes.c_int
+        L.itk_debug_mfma.argtypes = [I32, P, P, P, P]
+        L.itk_debug_fp8.argtypes = [P, P, P, I32, P]
+        L.itk_debug_coarse.argtypes = [P, P, P, I32, P]
+        _lib = L
+    return _lib
+
+
+def require_gpu():
+    """Raise unless the HIP library loads and a GPU is visible."""
+    import torch
+    lib()
+    if not torch.cuda.is_available():
+        raise RuntimeError("no HIP device visible: the itk kernels need an MI355X (gfx950)")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise ITKError(status, what)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    m = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.float8_e4m3fn: FP8_E4M3}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+# ------------------------------------------------------------------ ragged
+def topk_ragged_workspace_size(M: int, pitch: int, k: int) -> int:
+    return int(lib().topk_ragged_workspace_size(M, pitch, k))
+
+
+def topk_ragged(scores, row_len, k: int, out_idx=None, workspace=None, stream=None):
+    """Exact Top-k of each ragged fp32 row; returns int32 [M, k] (set order, -1 pad)."""
+    import torch
+    assert scores.is_cuda and scores.dtype == torch.float32 and scores.dim() == 2
+    assert scores.stride(1) == 1
+    M, pitch = scores.shape[0], scores.stride(0)
+    if out_idx is None:
+        out_idx = torch.empty((M, k), dtype=torch.int32, device=scores.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, topk_ragged_workspace_size(M, pitch, k)), dtype=torch.uint8,
+                                device=scores.device)
+    st = lib().topk_ragged(_ptr(scores), pitch, _ptr(row_len), M, k, _ptr(out_idx), _ptr(workspace),
+                           workspace.numel(), _stream(stream))
+    _check(st, "topk_ragged")
+    return out_idx
+
+
+# ------------------------------------------------------------------- fused
+def fused_workspace_size(T, H, D, N, k, q_t, k_t, flags=0) -> int:
+    return int(lib().indexer_topk_fused_workspace_size(T, H, D, N, k, q_t, k_t, flags))
+
+
+def indexer_topk_fused(Q, K, W, kv_len, k: int, k_scale=None, flags: int = 0, out_idx=None, out_score=None,
+                       workspace=None, stream=None):
+    """Fused indexer score + exact Top-k.  Q [T,H,D], K [N,D] (bf16/f16/f32 or
+    float8_e4m3fn with k_scale [N]), W [T,H] fp32, kv_len [T] int32.
+    Returns (out_idx int32 [T,k], out_score fp32 [T,k])."""
+    import torch
+    T, H, D = Q.shape
+    N = K.shape[0]
+    q_t, k_t = _dtype_code(Q), _dtype_code(K)
+    if out_idx is None:
+        out_idx = torch.empty((T, k), dtype=torch.int32, device=Q.device)
+    if out_score is None:
+        out_score = torch.empty((T, k), dtype=torch.float32, device=Q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, fused_workspace_size(T, H, D, N, k, q_t, k_t, flags)),
+                                dtype=torch.uint8, device=Q.device)
+    st = lib().indexer_topk_fused(_ptr(Q), q_t, _ptr(K), k_t, _ptr(k_scale), _ptr(W), _ptr(kv_len), T, H, D, N,
+                                  k, flags, _ptr(out_idx), _ptr(out_score), _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    _check(st, "indexer_topk_fused")
+    return out_idx, out_score
+
+
+def fused_tensors(case, device="cuda"):
+    """Move a host case (raw bit arrays + dtype codes) to device tensors."""
+    import torch
+
+    def as_t(bits, code):
+        t = torch.from_numpy(np.ascontiguousarray(bits))
+        if code == F32:
+            return t.to(device)
+        if code == FP8_E4M3:
+            return t.to(device).view(torch.float8_e4m3fn)
+        t = t.view(torch.int16).to(device)
+        return t.view(torch.bfloat16 if code == BF16 else torch.float16)
+
+    Q = as_t(case.q_bits, case.q_dtype)
+    K = as_t(case.k_bits, case.k_dtype)
+    S = None if case.k_scale is None else torch.from_numpy(case.k_scale).to(device)
+    W = torch.from_numpy(np.ascontiguousarray(case.W)).to(device)
+    kv = torch.from_numpy(np.ascontiguousarray(case.kv_len, dtype=np.int32)).to(device)
+    return Q, K, S, W, kv
+
+
+# ------------------------------------------------------------------ knobs
+def set_plan_opts(sample_stride=0, rho=0.0, rho1=0.0, capacity=0, splits=0, force_route=0):
+    o = PlanOpts(sample_stride, rho, rho1, capacity, splits, force_route)
+    _check(lib().itk_set_plan_opts(ctypes.byref(o)), "itk_set_plan_opts")
+
+
+def reset_plan_opts():
+    _check(lib().itk_set_plan_opts(None), "itk_set_plan_opts")
+
+
+def set_route_buffer(t=None):
+    _check(lib().itk_set_route_buffer(_ptr(t), 0 if t is None else t.numel()), "itk_set_route_buffer")
+
+
+def profile_enable(on: bool = True):
+    _check(lib().itk_profile_enable(1 if on else 0), "itk_profile_enable")
+
+
+def profile_read():
+    """{stage: (total_ms, launches)} since the last read."""
+    n = 16
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    names = (ctypes.c_char_p * n)()
+    k = lib().itk_profile_read(ms, cnt, names, n)
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(k) if cnt[i]}
+
+
+# ------------------------------------------------------------ test probes
+def debug_mfma(mtype: int, a_frags, b_frags):
+    """One 32x32 MFMA on per-lane fragments; returns float32 [64, 16]."""
+    import torch
+    c = torch.empty((64, 16), dtype=torch.float32, device=a_frags.device)
+    _check(lib().itk_debug_mfma(mtype, _ptr(a_frags), _ptr(b_frags), _ptr(c), _stream(None)), "itk_debug_mfma")
+    return c
+
+
+def debug_fp8(codes):
+    import torch
+    bf = torch.empty(codes.numel(), dtype=torch.int16, device=codes.device)
+    hf = torch.empty(codes.numel(), dtype=torch.int16, device=codes.device)
+    _check(lib().itk_debug_fp8(_ptr(codes), _ptr(bf), _ptr(hf), codes.numel(), _stream(None)), "itk_debug_fp8")
+    return bf, hf
+
+
+def debug_coarse(x):
+    import torch
+    n = x.numel()
+    key = torch.empty(n, dtype=torch.int32, device=x.device)
+    ep = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check(lib().itk_debug_coarse(_ptr(x), _ptr(key), _ptr(ep), n, _stream(None)), "itk_debug_coarse")
+    return key, ep

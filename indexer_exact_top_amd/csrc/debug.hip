@@ -1,0 +1,76 @@
+// Test-only probes of the layouts and conversions the fused kernels rely on.
+#include "fused_impl.hpp"
+
+namespace itk {
+
+// One 32x32 MFMA: lane l loads its A and B fragments from a[l], b[l] and
+// stores its 16 accumulator values to c[l*16 .. l*16+15].
+template <int MT>
+__global__ void k_debug_mfma(const typename MTraits<MT>::frag *a, const typename MTraits<MT>::frag *b, float *c)
+{
+    const int l = threadIdx.x;
+    f32x16_t acc = f32x16_t{};
+    acc = mfma32<MT>(a[l], b[l], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[l * 16 + r] = acc[r];
+}
+
+__global__ void k_debug_fp8(const uint8_t *in, uint16_t *bf, uint16_t *hf, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        bf[i] = (uint16_t)fp8_to_bf16_bits(in[i]);
+        hf[i] = (uint16_t)fp8_to_f16_bits(in[i]);
+    }
+}
+
+__global__ void k_debug_coarse(const float *x, uint32_t *key, float *endpoint, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        key[i] = coarse_key(x[i]);
+        endpoint[i] = coarse_endpoint((uint32_t)i);
+    }
+}
+
+}  // namespace itk
+
+using namespace itk;
+
+extern "C" {
+
+itk_status itk_debug_mfma(int32_t mtype, const void *a_frags, const void *b_frags, float *c_out, void *stream)
+{
+    if (!a_frags || !b_frags || !c_out) return ITK_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mtype == M_BF16)
+        hipLaunchKernelGGL(k_debug_mfma<M_BF16>, dim3(1), dim3(64), 0, s,
+                           static_cast<const u32x4_t *>(a_frags), static_cast<const u32x4_t *>(b_frags), c_out);
+    else if (mtype == M_F16)
+        hipLaunchKernelGGL(k_debug_mfma<M_F16>, dim3(1), dim3(64), 0, s,
+                           static_cast<const u32x4_t *>(a_frags), static_cast<const u32x4_t *>(b_frags), c_out);
+    else if (mtype == M_F32)
+        hipLaunchKernelGGL(k_debug_mfma<M_F32>, dim3(1), dim3(64), 0, s,
+                           static_cast<const float *>(a_frags), static_cast<const float *>(b_frags), c_out);
+    else
+        return ITK_ERR_INVALID_ARG;
+    return hipGetLastError() == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+}
+
+itk_status itk_debug_fp8(const uint8_t *in, uint16_t *bf16_out, uint16_t *f16_out, int32_t n, void *stream)
+{
+    if (!in || !bf16_out || !f16_out || n <= 0) return ITK_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(k_debug_fp8, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), in,
+                       bf16_out, f16_out, n);
+    return hipGetLastError() == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+}
+
+itk_status itk_debug_coarse(const float *x, uint32_t *key_out, float *endpoint_out, int32_t n, void *stream)
+{
+    if (!x || !key_out || !endpoint_out || n <= 0 || n > NBINS) return ITK_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(k_debug_coarse, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), x,
+                       key_out, endpoint_out, n);
+    return hipGetLastError() == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,808 @@
+// Fused lightning-indexer score + exact Top-k (gfx950), templated on the
+// operand formats and the shape class.
+//
+// Score (LiteTopK, arXiv 2607.11976, Sec. 2.1 Eq. (1)):
+//     s[t,j] = sum_h w[t,h] * ReLU(q[t,h,:] . k[j,:])
+// computed without materializing the score matrix, then selected exactly.
+//
+// Mapping onto CDNA4 (one wavefront owns one query, FUSED_WAVES queries per
+// workgroup share every staged key tile):
+//  * contraction: v_mfma_f32_32x32x16_{bf16,f16} (v_mfma_f32_32x32x2f32 for
+//    fp32 inputs).  MFMA rows are the query's heads (one or two 32-head
+//    blocks), columns are 32 keys; the query's Q fragments stay in VGPRs for
+//    the whole scan, K tiles of 64 keys are staged once per workgroup into a
+//    padded, double-buffered LDS tile (FP8 keys are widened to the MFMA
+//    operand type while staging; the per-key scale is applied after the head
+//    reduction, which is exact for non-negative scales).
+//  * epilogue in registers: each lane owns 16 head rows of one key column per
+//    32x32 block; w * max(acc, 0) is accumulated in-lane and the two half-waves
+//    are combined with one cross-lane exchange, leaving lane l with the score
+//    of key tile_start + l.
+//  * sample -> filter -> refresh -> select (LiteTopK Sec. 3.2): a tile-strided
+//    view of each row is scored first (two light passes: score range, then an
+//    equal-width histogram of m = 2048 bins over [s_min, s_max]); the
+//    threshold bin starts at the bin of the sample's rank-q score, q sized
+//    for rho * k of the row (the rank calibration of the Sample-Guided paper,
+//    Sec. 4.2).  In the scan, bin = floor((s - s_min) * delta) is one FMA; a
+//    key passes if its bin is not below the threshold bin; passing keys are
+//    compacted with a wave ballot + popcount + lane rank into a per-wave LDS
+//    staging list that is flushed 64 entries at a time with one atomic on the
+//    row's candidate tail, and counted in the wave's LDS histogram; every few
+//    tiles the wave recomputes the threshold bin from its histogram.
+//  * select: one workgroup per row runs the exact composite-key radix
+//    refinement over the row's candidates; rows whose candidates overflowed
+//    the buffer or fell short of k are re-scored from Q and K and selected
+//    exactly from the full row (recovery), so sampling never decides the
+//    result.
+#pragma once
+
+#include "itk_device.hpp"
+#include "itk_internal.hpp"
+
+namespace itk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+enum MType { M_BF16 = 0, M_F16 = 1, M_F32 = 2 };
+
+template <int MT>
+struct MTraits;
+template <>
+struct MTraits<M_BF16> {
+    using frag = u32x4_t;
+    static constexpr int ebytes = 2, kstep = 16, pad = 16;
+};
+template <>
+struct MTraits<M_F16> {
+    using frag = u32x4_t;
+    static constexpr int ebytes = 2, kstep = 16, pad = 16;
+};
+template <>
+struct MTraits<M_F32> {
+    using frag = float;
+    static constexpr int ebytes = 4, kstep = 2, pad = 16;
+};
+
+template <int MT>
+__device__ __forceinline__ f32x16_t mfma32(typename MTraits<MT>::frag a, typename MTraits<MT>::frag b, f32x16_t c)
+{
+    if constexpr (MT == M_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else if constexpr (MT == M_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// e4m3fn byte -> bf16 / fp16 bits (exact; both formats hold every e4m3fn value).
+__device__ __forceinline__ uint32_t fp8_to_bf16_bits(uint32_t b)
+{
+    const uint32_t s = (b & 0x80u) << 8, e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 15u && m == 7u) return s | 0x7FC0u;
+    if (e == 0u) return s | (__float_as_uint((float)m * 0x1p-9f) >> 16);
+    return s | ((e + 120u) << 7) | (m << 4);
+}
+__device__ __forceinline__ uint32_t fp8_to_f16_bits(uint32_t b)
+{
+    const uint32_t s = (b & 0x80u) << 8, e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 15u && m == 7u) return s | 0x7E00u;
+    if (e == 0u) return s | (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)((float)m * 0x1p-9f));
+    return s | ((e + 8u) << 10) | (m << 7);
+}
+
+// Kernel configuration: Q dtype, K dtype, head blocks, head dim, ReLU.
+template <int QT_, int KT_, int HB_, int D_, bool RELU_>
+struct FCfg {
+    static constexpr int QT = QT_, KT = KT_, HB = HB_, D = D_;
+    static constexpr bool RELU = RELU_;
+    static constexpr int MT = (QT == ITK_F32) ? M_F32 : (QT == ITK_BF16 ? M_BF16 : M_F16);
+    using TR = MTraits<MT>;
+    using frag = typename TR::frag;
+    static constexpr int KS = D / TR::kstep;                 // MFMA k-steps
+    static constexpr int ROWB = D * TR::ebytes + TR::pad;    // LDS bytes per staged key
+    static constexpr int TILE_BYTES = TILE_KEYS * ROWB;
+    static constexpr int kbytes = (KT == ITK_F32) ? 4 : (KT == ITK_FP8_E4M3 ? 1 : 2);
+    static constexpr int qbytes = (QT == ITK_F32) ? 4 : 2;
+    static constexpr bool SCALE = (KT == ITK_FP8_E4M3);
+    static constexpr int EPT = TILE_KEYS * D / FUSED_THREADS; // staged elements per thread
+};
+
+struct FusedArgs {
+    const void *Q;
+    const void *K;
+    const float *k_scale;
+    const float *W;
+    const int32_t *kv_len;
+    int32_t *out_idx;
+    float *out_score;
+    int32_t *route;
+    float4 *param;     // [T] {off, delta, degenerate, 0}
+    float2 *mm;        // [T][Ps] {min, max} of the sampled scores
+    uint32_t *hist;    // [T][NBINS] sample histogram
+    uint32_t *tail;    // [T] candidates appended (may exceed cap)
+    Cand *cand;        // [T][cap]
+    int64_t N, span, span_s;
+    int32_t T, H, k, cap, G, P, Ps, sample_tiles, force;
+    float rho;
+};
+
+__device__ __forceinline__ uint32_t kv_length(const FusedArgs &a, int t)
+{
+    int64_t L = a.kv_len[t];
+    if (L < 0) L = 0;
+    if (L > a.N) L = a.N;
+    return (uint32_t)L;
+}
+
+__device__ __forceinline__ void map_group_split(int b, int G, int P, int &g, int &p)
+{
+    if (P % 8 == 0) {  // XCD-aware: the workgroups of one key split share an XCD (and its L2)
+        const int xcd = b & 7, local = b >> 3;
+        p = (local / G) * 8 + xcd;
+        g = local % G;
+    } else {
+        g = b / P;
+        p = b % P;
+    }
+}
+
+// Number of sampled keys below L and the sample rank for the row.
+struct RowSample {
+    uint32_t n_a;
+    bool admit_all;
+    uint32_t q0;
+};
+__device__ __forceinline__ RowSample row_sample(const FusedArgs &a, int g, uint32_t L, bool degenerate)
+{
+    RowSample rs;
+    const uint32_t st = (uint32_t)a.sample_tiles, phase = (uint32_t)g % st;
+    const uint32_t nt = (L + TILE_KEYS - 1) / TILE_KEYS;
+    const uint32_t ns = nt > phase ? (nt - 1u - phase) / st + 1u : 0u;
+    rs.n_a = 0;
+    if (ns) {
+        const uint32_t last = (phase + (ns - 1u) * st) * TILE_KEYS;
+        rs.n_a = (ns - 1u) * TILE_KEYS + ((L - last) < (uint32_t)TILE_KEYS ? (L - last) : (uint32_t)TILE_KEYS);
+    }
+    const double target = (double)a.rho * (double)a.k;
+    rs.q0 = L ? (uint32_t)ceil(target * (double)rs.n_a / (double)L) : 0u;
+    rs.admit_all = degenerate || target >= (double)L || rs.n_a == 0u || rs.q0 == 0u || rs.q0 > rs.n_a;
+    return rs;
+}
+
+// ----------------------------------------------------------- fragments
+template <class C>
+struct QFrags {
+    typename C::frag q[C::HB][C::KS];
+    float w[C::HB][16];
+
+    __device__ void load(const FusedArgs &a, int t)
+    {
+        const int l = (int)lane_id();
+        const int H = a.H;
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb) {
+            const int head = hb * 32 + (l & 31);
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk) {
+                if constexpr (C::MT == M_F32) {
+                    const int d = kk * 2 + (l >> 5);
+                    q[hb][kk] = head < H ? static_cast<const float *>(a.Q)[((size_t)t * H + head) * C::D + d] : 0.f;
+                } else {
+                    const int d0 = kk * 16 + 8 * (l >> 5);
+                    const char *ptr = static_cast<const char *>(a.Q) + (((size_t)t * H + head) * C::D + d0) * 2;
+                    q[hb][kk] = head < H ? *reinterpret_cast<const u32x4_t *>(ptr) : u32x4_t{0u, 0u, 0u, 0u};
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int h = hb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+                w[hb][r] = h < H ? a.W[(size_t)t * H + h] : 0.f;
+            }
+        }
+    }
+};
+
+// Register epilogue: per lane, sum over its head rows of w * ReLU(acc), then
+// combine the two half-waves so that lane l holds the score of key column
+// l of block 0 (l < 32) or l - 32 of block 1 (l >= 32).
+template <class C>
+__device__ __forceinline__ float reduce_heads(const f32x16_t (&acc)[2][C::HB], const float (&w)[C::HB][16])
+{
+    float part[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        float s = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float x = acc[kb][hb][r];
+                s = fmaf(w[hb][r], C::RELU ? fmaxf(x, 0.f) : x, s);
+            }
+        part[kb] = s;
+    }
+    const bool lo = lane_id() < 32u;
+    const float other = __shfl_xor(lo ? part[1] : part[0], 32);
+    return (lo ? part[0] : part[1]) + other;
+}
+
+// Scores of 64 keys from a staged LDS tile: lane l gets key tile_start + l.
+template <class C>
+__device__ __forceinline__ float tile_scores_lds(const QFrags<C> &qf, const char *ktile)
+{
+    const int l = (int)lane_id();
+    f32x16_t acc[2][C::HB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb) acc[kb][hb] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const char *row = ktile + (kb * 32 + (l & 31)) * C::ROWB;
+            typename C::frag b;
+            if constexpr (C::MT == M_F32)
+                b = *reinterpret_cast<const float *>(row + (kk * 2 + (l >> 5)) * 4);
+            else
+                b = *reinterpret_cast<const u32x4_t *>(row + (kk * 16 + 8 * (l >> 5)) * 2);
+#pragma unroll
+            for (int hb = 0; hb < C::HB; ++hb) acc[kb][hb] = mfma32<C::MT>(qf.q[hb][kk], b, acc[kb][hb]);
+        }
+    }
+    return reduce_heads<C>(acc, qf.w);
+}
+
+// Same, with B fragments read straight from global K (recovery path).
+template <class C>
+__device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int64_t key0)
+{
+    const int l = (int)lane_id();
+    f32x16_t acc[2][C::HB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb) acc[kb][hb] = f32x16_t{};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int64_t key = key0 + kb * 32 + (l & 31);
+        const bool ok = key < a.N;
+        const char *krow = static_cast<const char *>(a.K) + (size_t)(ok ? key : 0) * C::D * C::kbytes;
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk) {
+            typename C::frag b;
+            if constexpr (C::MT == M_F32) {
+                b = ok ? reinterpret_cast<const float *>(krow)[kk * 2 + (l >> 5)] : 0.f;
+            } else if constexpr (C::KT == ITK_FP8_E4M3) {
+                const int d0 = kk * 16 + 8 * (l >> 5);
+                const u32x2_t raw = ok ? *reinterpret_cast<const u32x2_t *>(krow + d0) : u32x2_t{0u, 0u};
+                u32x4_t v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t word = raw[e >> 1];
+                    const uint32_t b0 = (word >> (16 * (e & 1))) & 0xFFu, b1 = (word >> (16 * (e & 1) + 8)) & 0xFFu;
+                    const uint32_t h0 = C::MT == M_BF16 ? fp8_to_bf16_bits(b0) : fp8_to_f16_bits(b0);
+                    const uint32_t h1 = C::MT == M_BF16 ? fp8_to_bf16_bits(b1) : fp8_to_f16_bits(b1);
+                    v[e] = h0 | (h1 << 16);
+                }
+                b = v;
+            } else {
+                const int d0 = kk * 16 + 8 * (l >> 5);
+                b = ok ? *reinterpret_cast<const u32x4_t *>(krow + d0 * 2) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int hb = 0; hb < C::HB; ++hb) acc[kb][hb] = mfma32<C::MT>(qf.q[hb][kk], b, acc[kb][hb]);
+        }
+    }
+    return reduce_heads<C>(acc, qf.w);
+}
+
+// ---------------------------------------------------- tile staging (LDS)
+// Each of the FUSED_THREADS threads moves EPT consecutive elements of one key
+// (thread -> key tid/8, part tid%8), widening FP8 to the MFMA operand type.
+template <class C>
+struct KStage {
+    static constexpr int RB = C::EPT * C::kbytes;  // raw bytes per thread
+    static constexpr int NV = RB >= 16 ? RB / 16 : 1;
+    u32x4_t v[NV];
+    u32x2_t v2;
+
+    __device__ void load(const FusedArgs &a, int64_t key0)
+    {
+        const int tid = threadIdx.x;
+        const int64_t key = key0 + (tid >> 3);
+        const int part = tid & 7;
+        const bool ok = key < a.N;
+        const char *src = static_cast<const char *>(a.K) + ((size_t)(ok ? key : 0) * C::D + part * C::EPT) * C::kbytes;
+        if constexpr (RB >= 16) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                v[i] = ok ? reinterpret_cast<const u32x4_t *>(src)[i] : u32x4_t{0u, 0u, 0u, 0u};
+        } else {
+            v2 = ok ? *reinterpret_cast<const u32x2_t *>(src) : u32x2_t{0u, 0u};
+        }
+    }
+
+    __device__ void store(char *ktile) const
+    {
+        const int tid = threadIdx.x;
+        char *dst = ktile + (tid >> 3) * C::ROWB + (tid & 7) * C::EPT * C::TR::ebytes;
+        if constexpr (C::KT == ITK_FP8_E4M3) {
+            // EPT fp8 bytes -> EPT 16-bit values
+            constexpr int OUTV = C::EPT * 2 / 16;
+            uint32_t words[C::EPT / 4];
+            if constexpr (RB >= 16) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) words[i * 4 + j] = v[i][j];
+            } else {
+                words[0] = v2[0];
+                words[1] = v2[1];
+            }
+#pragma unroll
+            for (int o = 0; o < OUTV; ++o) {
+                u32x4_t out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t word = words[o * 2 + (e >> 1)];
+                    const uint32_t b0 = (word >> (16 * (e & 1))) & 0xFFu, b1 = (word >> (16 * (e & 1) + 8)) & 0xFFu;
+                    const uint32_t h0 = C::MT == M_BF16 ? fp8_to_bf16_bits(b0) : fp8_to_f16_bits(b0);
+                    const uint32_t h1 = C::MT == M_BF16 ? fp8_to_bf16_bits(b1) : fp8_to_f16_bits(b1);
+                    out[e] = h0 | (h1 << 16);
+                }
+                reinterpret_cast<u32x4_t *>(dst)[o] = out;
+            }
+        } else {
+            if constexpr (RB >= 16) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i) reinterpret_cast<u32x4_t *>(dst)[i] = v[i];
+            } else {
+                *reinterpret_cast<u32x2_t *>(dst) = v2;
+            }
+        }
+    }
+};
+
+// Wave-level search: the largest bin b with sum_{b' >= b} hist[b'] >= q,
+// or -1 when the histogram holds fewer than q items.  Lane l owns bins
+// [NBINS - 32(l+1), NBINS - 32 l).
+template <class HistPtr>
+__device__ int wave_top_bin(HistPtr hist, uint32_t q)
+{
+    const int l = (int)lane_id();
+    const int hi = NBINS - 32 * l;  // exclusive
+    uint32_t c[32];
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        c[i] = hist[hi - 1 - i];
+        s += c[i];
+    }
+    uint32_t incl = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (l >= off) incl += o;
+    }
+    const uint64_t m = __ballot(incl >= q);
+    if (!m) return -1;
+    const int f = __ffsll((unsigned long long)m) - 1;
+    int bin = 0;
+    if (l == f) {
+        uint32_t cum = incl - s;
+        bin = hi - 32;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if (cum + c[i] >= q) { bin = hi - 1 - i; break; }
+            cum += c[i];
+        }
+    }
+    return __shfl(bin, f);
+}
+
+// Keys of sampled tile number `m` (0-based within the split's sampled tiles).
+struct SampleIter {
+    int64_t first_key;  // key of the first sampled tile in the split, or -1
+    int64_t stride_keys;
+    int64_t end;        // exclusive key bound for the split
+};
+__device__ __forceinline__ SampleIter sample_iter(const FusedArgs &a, int g, int p, uint32_t maxL)
+{
+    SampleIter it;
+    const int64_t st = a.sample_tiles, phase = g % a.sample_tiles;
+    const int64_t lo = (int64_t)p * a.span_s;
+    int64_t hi = lo + a.span_s;
+    if (hi > (int64_t)maxL) hi = maxL;
+    it.stride_keys = st * TILE_KEYS;
+    it.end = hi;
+    const int64_t t0 = lo / TILE_KEYS;  // first tile of the split (lo is tile aligned)
+    int64_t first = t0 + ((phase - t0 % st) % st + st) % st;
+    it.first_key = first * TILE_KEYS < hi ? first * TILE_KEYS : -1;
+    return it;
+}
+
+template <class C>
+struct FusedSmem {
+    char ktile[2][C::TILE_BYTES];
+    uint32_t whist[FUSED_WAVES][NBINS];
+    Cand stage[FUSED_WAVES][128];
+    uint32_t maxL;
+};
+
+__device__ __forceinline__ uint32_t group_max_len(const FusedArgs &a, int g)
+{
+    uint32_t m = 0;
+    for (int w = 0; w < FUSED_WAVES; ++w) {
+        const int t = g * FUSED_WAVES + w;
+        if (t < a.T) {
+            const uint32_t L = kv_length(a, t);
+            m = L > m ? L : m;
+        }
+    }
+    return m;
+}
+
+// -------------------------------------------- sample pass A: score range
+template <class C>
+__global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
+{
+    __shared__ char ktile[C::TILE_BYTES];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int g, p;
+    map_group_split(blockIdx.x, a.G, a.Ps, g, p);
+    const int t = g * FUSED_WAVES + wave;
+    const bool active = t < a.T;
+    const uint32_t L = active ? kv_length(a, t) : 0u;
+    if (p == 0 && active) {  // per-call reset of the row's counters
+        for (int i = lane; i < NBINS; i += 64) a.hist[(size_t)t * NBINS + i] = 0u;
+        if (lane == 0) a.tail[t] = 0u;
+    }
+    const uint32_t maxL = group_max_len(a, g);
+    const SampleIter it = sample_iter(a, g, p, maxL);
+    QFrags<C> qf;
+    if (active) qf.load(a, t);
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    if (it.first_key >= 0 && a.force != 1) {
+        for (int64_t key0 = it.first_key; key0 < it.end; key0 += it.stride_keys) {
+            KStage<C> ks;
+            ks.load(a, key0);
+            __syncthreads();
+            ks.store(ktile);
+            __syncthreads();
+            if (active && key0 < (int64_t)L) {
+                float s = tile_scores_lds<C>(qf, ktile);
+                const int64_t key = key0 + lane;
+                if (key < (int64_t)L) {
+                    if constexpr (C::SCALE) s *= a.k_scale[key];
+                    mn = fminf(mn, s);
+                    mx = fmaxf(mx, s);
+                }
+            }
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            mn = fminf(mn, __shfl_xor(mn, off));
+            mx = fmaxf(mx, __shfl_xor(mx, off));
+        }
+        if (lane == 0) a.mm[(size_t)t * a.Ps + p] = make_float2(mn, mx);
+    }
+}
+
+// Equal-width bin mapping from the sampled score range (m = NBINS bins).
+__device__ __forceinline__ float4 bin_params(const FusedArgs &a, int t)
+{
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    for (int p = 0; p < a.Ps; ++p) {
+        const float2 v = a.mm[(size_t)t * a.Ps + p];
+        mn = fminf(mn, v.x);
+        mx = fmaxf(mx, v.y);
+    }
+    const float delta = (float)NBINS / (mx - mn);
+    const bool ok = (mx > mn) && __builtin_isfinite(delta) && delta > 0.f && __builtin_isfinite(mn);
+    return ok ? make_float4(-mn * delta, delta, 0.f, 0.f) : make_float4(0.f, 0.f, 1.f, 0.f);
+}
+
+__device__ __forceinline__ uint32_t bin_of(float b)
+{
+    return (uint32_t)fminf(fmaxf(floorf(b), 0.f), (float)(NBINS - 1));
+}
+
+// ---------------------------------------- sample pass B: sample histogram
+template <class C>
+__global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
+{
+    __shared__ char ktile[C::TILE_BYTES];
+    __shared__ uint32_t whist[FUSED_WAVES][NBINS];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int g, p;
+    map_group_split(blockIdx.x, a.G, a.Ps, g, p);
+    const int t = g * FUSED_WAVES + wave;
+    const bool active = t < a.T;
+    const uint32_t L = active ? kv_length(a, t) : 0u;
+    for (int i = lane; i < NBINS; i += 64) whist[wave][i] = 0u;
+    float4 bp = make_float4(0.f, 0.f, 1.f, 0.f);
+    if (active) {
+        bp = bin_params(a, t);
+        if (p == 0 && lane == 0) a.param[t] = bp;
+    }
+    const uint32_t maxL = group_max_len(a, g);
+    const SampleIter it = sample_iter(a, g, p, maxL);
+    QFrags<C> qf;
+    if (active) qf.load(a, t);
+    if (it.first_key >= 0 && a.force != 1) {
+        for (int64_t key0 = it.first_key; key0 < it.end; key0 += it.stride_keys) {
+            KStage<C> ks;
+            ks.load(a, key0);
+            __syncthreads();
+            ks.store(ktile);
+            __syncthreads();
+            if (active && key0 < (int64_t)L && bp.z == 0.f) {
+                float s = tile_scores_lds<C>(qf, ktile);
+                const int64_t key = key0 + lane;
+                if (key < (int64_t)L) {
+                    if constexpr (C::SCALE) s *= a.k_scale[key];
+                    atomicAdd(&whist[wave][bin_of(fmaf(s, bp.y, bp.x))], 1u);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (active && bp.z == 0.f) {
+        for (int i = lane; i < NBINS; i += 64) {
+            const uint32_t c = whist[wave][i];
+            if (c) atomicAdd(&a.hist[(size_t)t * NBINS + i], c);
+        }
+    }
+}
+
+// ------------------------------------------------ main pass: filter scan
+constexpr int REFRESH_TILES = 8;
+
+template <class C>
+__global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
+{
+    __shared__ FusedSmem<C> sm;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int g, p;
+    map_group_split(blockIdx.x, a.G, a.P, g, p);
+    if (a.force == 1) return;  // every row takes the re-scoring route
+    const int t = g * FUSED_WAVES + wave;
+    const bool active = t < a.T;
+    const uint32_t L = active ? kv_length(a, t) : 0u;
+    const uint32_t maxL = group_max_len(a, g);
+    const int64_t k_lo = (int64_t)p * a.span;
+    int64_t k_hi = k_lo + a.span;
+    if (k_hi > (int64_t)maxL) k_hi = maxL;
+    const int ntiles = k_hi > k_lo ? (int)((k_hi - k_lo + TILE_KEYS - 1) / TILE_KEYS) : 0;
+
+    uint32_t *whist = sm.whist[wave];
+    Cand *stage = sm.stage[wave];
+    for (int i = lane; i < NBINS; i += 64) whist[i] = 0u;
+
+    // Initial threshold bin from the sample (wave-uniform state).
+    float off = 0.f, delta = 0.f;
+    int gate_bin = 0;
+    float gate_f = -__builtin_inff();
+    if (active) {
+        const float4 bp = a.param[t];
+        const RowSample rs = row_sample(a, g, L, bp.z != 0.f);
+        if (!rs.admit_all) {
+            off = bp.x;
+            delta = bp.y;
+            const int b = wave_top_bin(a.hist + (size_t)t * NBINS, rs.q0);
+            gate_bin = b > 0 ? b : 0;
+            gate_f = gate_bin > 0 ? (float)gate_bin : -__builtin_inff();
+        }
+    }
+    QFrags<C> qf;
+    if (active) qf.load(a, t);
+    uint32_t stage_n = 0, admitted = 0;
+    Cand *cand = a.cand + (size_t)(active ? t : 0) * a.cap;
+    const uint32_t cap = (uint32_t)a.cap;
+
+    auto flush = [&](uint32_t n) {
+        uint32_t slot = 0;
+        if (lane == 0) slot = atomicAdd(&a.tail[t], n);
+        slot = __shfl(slot, 0);
+        if ((uint32_t)lane < n && slot + lane < cap) cand[slot + lane] = stage[lane];
+    };
+
+    KStage<C> ks;
+    if (ntiles > 0) {
+        ks.load(a, k_lo);
+        ks.store(sm.ktile[0]);
+    }
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int64_t key0 = k_lo + (int64_t)it * TILE_KEYS;
+        if (it + 1 < ntiles) ks.load(a, key0 + TILE_KEYS);
+        if (active && key0 < (int64_t)L) {
+            float s = tile_scores_lds<C>(qf, sm.ktile[it & 1]);
+            const int64_t key = key0 + lane;
+            const bool valid = key < (int64_t)L;
+            if constexpr (C::SCALE) s *= valid ? a.k_scale[valid ? key : 0] : 0.f;
+            const float b = fmaf(s, delta, off);
+            const bool pass = valid && b >= gate_f;
+            const uint64_t m = __ballot(pass);
+            if (m) {
+                const uint32_t pos = stage_n + lanes_below(m);
+                if (pass) {
+                    atomicAdd(&whist[bin_of(b)], 1u);
+                    stage[pos] = Cand{(uint32_t)key, s};
+                }
+                const uint32_t n = (uint32_t)__popcll(m);
+                stage_n += n;
+                admitted += n;
+                if (stage_n >= 64u) {
+                    flush(64u);
+                    const bool mv = (uint32_t)lane < stage_n - 64u;
+                    Cand e;
+                    if (mv) e = stage[64 + lane];
+                    if (mv) stage[lane] = e;
+                    stage_n -= 64u;
+                }
+            }
+            if ((it % REFRESH_TILES) == REFRESH_TILES - 1 && admitted >= (uint32_t)a.k && delta > 0.f) {
+                // Threshold refresh: the bin holding the k-th largest score
+                // seen so far is a lower bound of the row's k-th largest bin.
+                const int T = wave_top_bin(whist, (uint32_t)a.k);
+                if (T > gate_bin) {
+                    gate_bin = T;
+                    gate_f = (float)gate_bin;
+                }
+            }
+        }
+        if (it + 1 < ntiles) ks.store(sm.ktile[(it + 1) & 1]);
+        __syncthreads();
+    }
+    if (active && stage_n) flush(stage_n);
+}
+
+// ------------------------------------------- select (+ recovery) per row
+struct CandSrc {
+    const Cand *c;
+    uint32_t n;
+    template <class F>
+    __device__ void for_each(F &&f) const
+    {
+        for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+            const Cand e = c[i];
+            f(e.idx, e.val);
+        }
+    }
+};
+
+// Re-scores every valid key of row t (each wave takes every 4th tile, with
+// B fragments read straight from global memory).
+template <class C>
+struct RescoreSrc {
+    const FusedArgs *a;
+    int t;
+    uint32_t L;
+    template <class F>
+    __device__ void for_each(F &&f) const
+    {
+        const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+        const int lane = (int)lane_id();
+        QFrags<C> qf;
+        qf.load(*a, t);
+        for (int64_t key0 = (int64_t)wave * TILE_KEYS; key0 < (int64_t)L; key0 += (int64_t)nw * TILE_KEYS) {
+            float s = tile_scores_global<C>(qf, *a, key0);
+            const int64_t key = key0 + lane;
+            if (key < (int64_t)L) {
+                if constexpr (C::SCALE) s *= a->k_scale[key];
+                f((uint32_t)key, s);
+            }
+        }
+    }
+};
+
+enum { FROUTE_SAMPLE = 1, FROUTE_RECOVER = 3, FROUTE_ALL = 4 };
+
+template <class C>
+__global__ __launch_bounds__(SEL_THREADS) void k_fused_select(FusedArgs a)
+{
+    __shared__ SelectSmem sm;
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x;
+    const uint32_t L = kv_length(a, t);
+    const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+    int32_t *oi = a.out_idx + (size_t)t * a.k;
+    float *os = a.out_score + (size_t)t * a.k;
+    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += SEL_THREADS) {
+        oi[i] = -1;
+        os[i] = -__builtin_inff();
+    }
+    if (need == 0) {
+        if (tid == 0 && a.route) a.route[t] = FROUTE_ALL;
+        return;
+    }
+    const uint32_t n = a.tail[t];
+    const bool recover = a.force == 1 || n > (uint32_t)a.cap || n < need;
+    auto emit = [&](uint32_t slot, uint64_t K) {
+        if (slot < need) {
+            oi[slot] = (int32_t)key_index(K);
+            os[slot] = key_value(K);
+        }
+    };
+    if (!recover) {
+        CandSrc src{a.cand + (size_t)t * a.cap, n};
+        exact_select<SEL_THREADS>(sm, src, need, emit);
+    } else {
+        RescoreSrc<C> src{&a, t, L};
+        exact_select<SEL_THREADS>(sm, src, need, emit);
+    }
+    if (tid == 0 && a.route) {
+        const float4 bp = a.param[t];
+        const RowSample rs = row_sample(a, t / FUSED_WAVES, L, bp.z != 0.f);
+        a.route[t] = recover ? FROUTE_RECOVER : (rs.admit_all ? FROUTE_ALL : FROUTE_SAMPLE);
+    }
+}
+
+// --------------------------------------------------------------- launch
+template <class C>
+hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t stream)
+{
+    {
+        StageTimer st(ST_F_MINMAX, stream);
+        hipLaunchKernelGGL(k_fused_minmax<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), 0, stream, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    {
+        StageTimer st(ST_F_HIST, stream);
+        hipLaunchKernelGGL(k_fused_samplehist<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), 0, stream, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        StageTimer st(ST_F_MAIN, stream);
+        hipLaunchKernelGGL(k_fused_main<C>, dim3(p.G * p.P), dim3(FUSED_THREADS), 0, stream, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        StageTimer st(ST_F_SELECT, stream);
+        hipLaunchKernelGGL(k_fused_select<C>, dim3(p.T), dim3(SEL_THREADS), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+using FusedLauncher = hipError_t (*)(const FusedPlan &, const FusedArgs &, hipStream_t);
+
+// Registry of instantiated configurations (filled by the per-dtype units).
+FusedLauncher find_fused_launcher(int qt, int kt, int hb, int d, bool relu);
+
+#define ITK_FUSED_CASES_FOR(QT, KT)                                                               \
+    if (qt == QT && kt == KT) {                                                                   \
+        if (relu) {                                                                               \
+            if (hb == 1 && d == 64) return &launch_fused_cfg<FCfg<QT, KT, 1, 64, true>>;          \
+            if (hb == 1 && d == 128) return &launch_fused_cfg<FCfg<QT, KT, 1, 128, true>>;        \
+            if (hb == 1 && d == 256) return &launch_fused_cfg<FCfg<QT, KT, 1, 256, true>>;        \
+            if (hb == 2 && d == 64) return &launch_fused_cfg<FCfg<QT, KT, 2, 64, true>>;          \
+            if (hb == 2 && d == 128) return &launch_fused_cfg<FCfg<QT, KT, 2, 128, true>>;        \
+        } else {                                                                                  \
+            if (hb == 1 && d == 64) return &launch_fused_cfg<FCfg<QT, KT, 1, 64, false>>;         \
+            if (hb == 1 && d == 128) return &launch_fused_cfg<FCfg<QT, KT, 1, 128, false>>;       \
+            if (hb == 1 && d == 256) return &launch_fused_cfg<FCfg<QT, KT, 1, 256, false>>;       \
+        }                                                                                         \
+    }
+
+// fp32 operands: ceil(H/32) * D <= 128 keeps the Q fragments within budget.
+#define ITK_FUSED_CASES_F32                                                                       \
+    if (qt == ITK_F32 && kt == ITK_F32) {                                                         \
+        if (hb == 1 && d == 64) return relu ? &launch_fused_cfg<FCfg<ITK_F32, ITK_F32, 1, 64, true>>        \
+                                            : &launch_fused_cfg<FCfg<ITK_F32, ITK_F32, 1, 64, false>>;      \
+        if (hb == 1 && d == 128) return relu ? &launch_fused_cfg<FCfg<ITK_F32, ITK_F32, 1, 128, true>>      \
+                                             : &launch_fused_cfg<FCfg<ITK_F32, ITK_F32, 1, 128, false>>;    \
+        if (hb == 2 && d == 64 && relu) return &launch_fused_cfg<FCfg<ITK_F32, ITK_F32, 2, 64, true>>;    \
+    }
+
+}  // namespace itk

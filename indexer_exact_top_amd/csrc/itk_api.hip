@@ -1,0 +1,281 @@
+// C ABI: argument validation, planning, workspace carving and launches.
+// Nothing here reads device data or allocates device memory.
+#include <math.h>
+#include <mutex>
+#include <vector>
+
+#include "fused_impl.hpp"
+#include "itk_internal.hpp"
+
+namespace itk {
+
+Knobs &knobs()
+{
+    static Knobs k;
+    return k;
+}
+
+RouteSink &route_sink()
+{
+    static RouteSink r;
+    return r;
+}
+
+FusedLauncher find_fused_launcher_bf16(int, int, int, int, bool);
+FusedLauncher find_fused_launcher_f16(int, int, int, int, bool);
+FusedLauncher find_fused_launcher_f32(int, int, int, int, bool);
+
+FusedLauncher find_fused_launcher(int qt, int kt, int hb, int d, bool relu)
+{
+    if (qt == ITK_BF16) return find_fused_launcher_bf16(qt, kt, hb, d, relu);
+    if (qt == ITK_F16) return find_fused_launcher_f16(qt, kt, hb, d, relu);
+    if (qt == ITK_F32) return find_fused_launcher_f32(qt, kt, hb, d, relu);
+    return nullptr;
+}
+
+// ---------------------------------------------------------- profiling
+namespace {
+struct ProfRec {
+    int stage;
+    hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+const char *const g_stage_names[ST_COUNT] = {"ragged_scan", "ragged_finish", "fused_sample_range",
+                                             "fused_sample_hist", "fused_main", "fused_select"};
+}  // namespace
+
+StageTimer::StageTimer(int stage_id, hipStream_t s) : stage(-1), stream(s)
+{
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    ProfRec r{stage_id, nullptr, nullptr};
+    if (hipEventCreate(&r.a) != hipSuccess) return;
+    if (hipEventCreate(&r.b) != hipSuccess) {
+        (void)hipEventDestroy(r.a);
+        return;
+    }
+    (void)hipEventRecord(r.a, stream);
+    g_prof.push_back(r);
+    stage = stage_id;
+}
+
+StageTimer::~StageTimer()
+{
+    if (stage < 0) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    (void)hipEventRecord(g_prof.back().b, stream);
+}
+
+static uint64_t ceil_div_u(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk_dtype qt, itk_dtype kt,
+                      uint32_t flags, FusedPlan *out)
+{
+    if (T <= 0 || H <= 0 || D <= 0 || N <= 0 || k <= 0) return ITK_ERR_INVALID_ARG;
+    if (N > (int64_t)0x7FFFFFFF) return ITK_ERR_UNSUPPORTED;
+    if (qt < ITK_F32 || qt > ITK_FP8_E4M3 || kt < ITK_F32 || kt > ITK_FP8_E4M3) return ITK_ERR_INVALID_ARG;
+    if (flags & ~ITK_FLAG_NO_RELU) return ITK_ERR_INVALID_ARG;
+    if ((flags & ITK_FLAG_NO_RELU) && H != 1) return ITK_ERR_INVALID_ARG;
+    if (H > 64) return ITK_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128 && D != 256) return ITK_ERR_UNSUPPORTED;
+    const bool pair_ok = (qt == ITK_BF16 && (kt == ITK_BF16 || kt == ITK_FP8_E4M3)) ||
+                         (qt == ITK_F16 && (kt == ITK_F16 || kt == ITK_FP8_E4M3)) ||
+                         (qt == ITK_F32 && kt == ITK_F32);
+    if (!pair_ok) return ITK_ERR_UNSUPPORTED;
+    const int HB = (H + 31) / 32;
+    if (HB == 2 && D > 128) return ITK_ERR_UNSUPPORTED;
+    if (qt == ITK_F32 && HB * D > 128) return ITK_ERR_UNSUPPORTED;
+    const bool relu = !(flags & ITK_FLAG_NO_RELU);
+    if (!find_fused_launcher(qt, kt, HB, D, relu)) return ITK_ERR_UNSUPPORTED;
+
+    const Knobs &kn = knobs();
+    FusedPlan p;
+    p.T = T; p.H = H; p.D = D; p.N = N; p.k = k; p.qt = qt; p.kt = kt; p.flags = flags; p.HB = HB;
+    p.G = (int32_t)ceil_div_u((uint64_t)T, FUSED_WAVES);
+    // Key splits: fill the 256 CUs with about one workgroup each; a split
+    // count that is a multiple of 8 places each split on one XCD.
+    int P = p.G >= 256 ? 1 : (int)ceil_div_u(256, (uint64_t)p.G);
+    if (P >= 8) P = (int)ceil_div_u((uint64_t)P, 8) * 8;
+    const int Pmax = (int)(N / 4096) > 1 ? (int)(N / 4096) : 1;
+    if (P > Pmax) P = Pmax;
+    if (kn.splits > 0) P = kn.splits;
+    int64_t span = (int64_t)ceil_div_u((uint64_t)N, (uint64_t)P);
+    span = (int64_t)ceil_div_u((uint64_t)span, TILE_KEYS) * TILE_KEYS;
+    P = (int)ceil_div_u((uint64_t)N, (uint64_t)span);
+    p.P = P; p.span = span;
+    p.Ps = P; p.span_s = span;
+    const int64_t ntiles = (int64_t)ceil_div_u((uint64_t)N, TILE_KEYS);
+    int st = (int)((ntiles + 31) / 32);
+    if (st < 1) st = 1;
+    if (st > 64) st = 64;
+    if (kn.sample_stride > 0) st = kn.sample_stride;
+    p.sample_tiles = st;
+    p.rho = kn.rho > 0.f ? kn.rho : 2.0f;
+    int cap = 4 * k > 2048 ? 4 * k : 2048;
+    if (kn.capacity > 0) cap = kn.capacity;
+    const int need_all = (int)ceil((double)p.rho * k);
+    if (cap < need_all) cap = need_all;
+    p.cap = cap;
+    p.force = kn.force_route;
+    size_t off = 0;
+    p.off_param = off; off = align256(off + (size_t)T * sizeof(float4));
+    p.off_mm = off; off = align256(off + (size_t)T * p.Ps * sizeof(float2));
+    p.off_hist = off; off = align256(off + (size_t)T * NBINS * sizeof(uint32_t));
+    p.off_tail = off; off = align256(off + (size_t)T * sizeof(uint32_t));
+    p.off_gate = off; off = align256(off + (size_t)T * sizeof(int32_t));
+    p.off_cand = off; off = align256(off + (size_t)T * cap * sizeof(Cand));
+    p.bytes = off;
+    *out = p;
+    return ITK_OK;
+}
+
+hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const float *k_scale, const float *W,
+                        const int32_t *kv_len, int32_t *out_idx, float *out_score, void *ws, hipStream_t stream)
+{
+    char *w = static_cast<char *>(ws);
+    FusedArgs a;
+    a.Q = Q; a.K = K; a.k_scale = k_scale; a.W = W; a.kv_len = kv_len;
+    a.out_idx = out_idx; a.out_score = out_score;
+    const RouteSink &rs = route_sink();
+    a.route = (rs.ptr && rs.rows >= p.T) ? rs.ptr : nullptr;
+    a.param = reinterpret_cast<float4 *>(w + p.off_param);
+    a.mm = reinterpret_cast<float2 *>(w + p.off_mm);
+    a.hist = reinterpret_cast<uint32_t *>(w + p.off_hist);
+    a.tail = reinterpret_cast<uint32_t *>(w + p.off_tail);
+    a.cand = reinterpret_cast<Cand *>(w + p.off_cand);
+    a.N = p.N; a.span = p.span; a.span_s = p.span_s;
+    a.T = p.T; a.H = p.H; a.k = p.k; a.cap = p.cap; a.G = p.G; a.P = p.P; a.Ps = p.Ps;
+    a.sample_tiles = p.sample_tiles; a.force = p.force; a.rho = p.rho;
+    FusedLauncher fn = find_fused_launcher(p.qt, p.kt, p.HB, p.D, !(p.flags & ITK_FLAG_NO_RELU));
+    if (!fn) return hipErrorInvalidValue;
+    return fn(p, a, stream);
+}
+
+}  // namespace itk
+
+using namespace itk;
+
+extern "C" {
+
+const char *itk_status_string(itk_status s)
+{
+    switch (s) {
+    case ITK_OK: return "ok";
+    case ITK_ERR_INVALID_ARG: return "invalid argument";
+    case ITK_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case ITK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case ITK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+size_t topk_ragged_workspace_size(int32_t M, int64_t row_pitch, int32_t k)
+{
+    if (M <= 0 || row_pitch <= 0 || k <= 0 || row_pitch > (int64_t)0x7FFFFFFF) return 0;
+    return plan_ragged(M, row_pitch, k).bytes;
+}
+
+itk_status topk_ragged(const float *scores, int64_t row_pitch, const int32_t *row_len, int32_t M, int32_t k,
+                       int32_t *out_idx, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!scores || !row_len || !out_idx) return ITK_ERR_INVALID_ARG;
+    if (M <= 0 || k <= 0 || row_pitch <= 0) return ITK_ERR_INVALID_ARG;
+    if (row_pitch > (int64_t)0x7FFFFFFF) return ITK_ERR_UNSUPPORTED;
+    const RaggedPlan p = plan_ragged(M, row_pitch, k);
+    if (!workspace || workspace_bytes < p.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return ITK_ERR_WORKSPACE;
+    const hipError_t e = launch_ragged(p, scores, row_len, out_idx, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+}
+
+size_t indexer_topk_fused_workspace_size(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk_dtype q_t,
+                                         itk_dtype k_t, uint32_t flags)
+{
+    FusedPlan p;
+    if (plan_fused(T, H, D, N, k, q_t, k_t, flags, &p) != ITK_OK) return 0;
+    return p.bytes;
+}
+
+itk_status indexer_topk_fused(const void *Q, itk_dtype q_t, const void *K, itk_dtype k_t, const float *k_scale,
+                              const float *W, const int32_t *kv_len, int32_t T, int32_t H, int32_t D, int64_t N,
+                              int32_t k, uint32_t flags, int32_t *out_idx, float *out_score, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    if (!Q || !K || !W || !kv_len || !out_idx || !out_score) return ITK_ERR_INVALID_ARG;
+    if ((k_t == ITK_FP8_E4M3) != (k_scale != nullptr)) return ITK_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(Q) & 15u) || (reinterpret_cast<uintptr_t>(K) & 15u)) return ITK_ERR_INVALID_ARG;
+    FusedPlan p;
+    const itk_status st = plan_fused(T, H, D, N, k, q_t, k_t, flags, &p);
+    if (st != ITK_OK) return st;
+    if (!workspace || workspace_bytes < p.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return ITK_ERR_WORKSPACE;
+    const hipError_t e = launch_fused(p, Q, K, k_scale, W, kv_len, out_idx, out_score, workspace,
+                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+}
+
+itk_status itk_set_plan_opts(const itk_plan_opts *o)
+{
+    Knobs &k = knobs();
+    if (!o) {
+        k = Knobs();
+        return ITK_OK;
+    }
+    if (o->sample_stride < 0 || o->capacity < 0 || o->splits < 0 || o->force_route < 0 || o->force_route > 2 ||
+        !(o->rho >= 0.f) || !(o->rho1 >= 0.f))
+        return ITK_ERR_INVALID_ARG;
+    if (o->sample_stride > 0 && o->sample_stride > 4096) return ITK_ERR_INVALID_ARG;
+    k.sample_stride = o->sample_stride;
+    k.rho = o->rho;
+    k.rho1 = o->rho1;
+    k.capacity = o->capacity;
+    k.splits = o->splits;
+    k.force_route = o->force_route;
+    return ITK_OK;
+}
+
+itk_status itk_set_route_buffer(int32_t *route_out, int32_t rows)
+{
+    if (route_out && rows <= 0) return ITK_ERR_INVALID_ARG;
+    route_sink().ptr = route_out;
+    route_sink().rows = route_out ? rows : 0;
+    return ITK_OK;
+}
+
+itk_status itk_profile_enable(int32_t on)
+{
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = on != 0;
+    return ITK_OK;
+}
+
+int32_t itk_profile_read(double *ms_out, int32_t *count_out, const char **names_out, int32_t max_stages)
+{
+    std::vector<ProfRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        recs.swap(g_prof);
+    }
+    double ms[ST_COUNT] = {0};
+    int32_t cnt[ST_COUNT] = {0};
+    for (const ProfRec &r : recs) {
+        float t = 0.f;
+        if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) {
+            ms[r.stage] += t;
+            cnt[r.stage] += 1;
+        }
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    const int n = max_stages < ST_COUNT ? max_stages : ST_COUNT;
+    for (int i = 0; i < n; ++i) {
+        if (ms_out) ms_out[i] = ms[i];
+        if (count_out) count_out[i] = cnt[i];
+        if (names_out) names_out[i] = g_stage_names[i];
+    }
+    return n;
+}
+
+}  // extern "C"

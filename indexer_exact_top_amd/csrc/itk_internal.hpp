@@ -1,0 +1,97 @@
+// Host-side plan structures and launchers shared by the API and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/itk.h"
+
+namespace itk {
+
+// Candidate record: the row index and its fp32 value.
+struct Cand {
+    uint32_t idx;
+    float val;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Planner knobs (process-global, tests only).
+struct Knobs {
+    int32_t sample_stride = 0;
+    float rho = 0.f, rho1 = 0.f;
+    int32_t capacity = 0;
+    int32_t splits = 0;
+    int32_t force_route = 0;
+};
+Knobs &knobs();
+
+struct RouteSink {
+    int32_t *ptr = nullptr;
+    int32_t rows = 0;
+};
+RouteSink &route_sink();
+
+// --------------------------------------------------------------- ragged
+constexpr int RAG_THREADS = 256;
+constexpr int RAG_WAVES = RAG_THREADS / 64;
+
+struct RaggedPlan {
+    int32_t M = 0;
+    int64_t pitch = 0;
+    int32_t k = 0;
+    int32_t P = 1;           // segments per row
+    int64_t seg = 0;         // segment length (multiple of 1024)
+    int32_t subcap = 0;      // candidate capacity per (segment, wave)
+    int32_t bandcap = 0;     // band candidates per row
+    int32_t view_blocks = 0; // view stride in 16-element blocks
+    float rho = 1.5f, rho1 = 1.75f;
+    int32_t force = 0;
+    // workspace carve
+    size_t off_cnt = 0, off_c1 = 0, off_ep = 0, off_slices = 0, off_band = 0, bytes = 0;
+};
+RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k);
+hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t *row_len,
+                         int32_t *out_idx, void *ws, hipStream_t stream);
+
+// ---------------------------------------------------------------- fused
+constexpr int FUSED_WAVES = 8;                  // queries per workgroup
+constexpr int FUSED_THREADS = FUSED_WAVES * 64;
+constexpr int TILE_KEYS = 64;
+constexpr int SEL_THREADS = 256;
+
+struct FusedPlan {
+    int32_t T = 0, H = 0, D = 0, k = 0;
+    int64_t N = 0;
+    itk_dtype qt = ITK_BF16, kt = ITK_BF16;
+    uint32_t flags = 0;
+    int32_t HB = 1;          // 32-head blocks
+    int32_t G = 0;           // query groups of FUSED_WAVES
+    int32_t P = 1;           // key splits (main pass)
+    int32_t Ps = 1;          // key splits (sample passes)
+    int64_t span = 0;        // keys per split (multiple of 64), main
+    int64_t span_s = 0;      // keys per split, sample
+    int32_t sample_tiles = 1;// sampled tile stride
+    float rho = 2.0f;
+    int32_t cap = 0;         // candidates per row
+    int32_t force = 0;
+    size_t off_param = 0, off_mm = 0, off_hist = 0, off_tail = 0, off_gate = 0, off_cand = 0, bytes = 0;
+};
+itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk_dtype qt, itk_dtype kt,
+                      uint32_t flags, FusedPlan *out);
+hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const float *k_scale,
+                        const float *W, const int32_t *kv_len, int32_t *out_idx, float *out_score,
+                        void *ws, hipStream_t stream);
+
+// ------------------------------------------------------------ profiling
+// Records an event pair around a launch when profiling is enabled.
+struct StageTimer {
+    int stage;
+    hipStream_t stream;
+    StageTimer(int stage_id, hipStream_t s);
+    ~StageTimer();
+};
+enum Stage { ST_RAG_SCAN = 0, ST_RAG_FINISH, ST_F_MINMAX, ST_F_HIST, ST_F_MAIN, ST_F_SELECT, ST_COUNT };
+
+}  // namespace itk

@@ -1,0 +1,362 @@
+// Standalone exact Top-k over materialized ragged fp32 rows (gfx950).
+//
+// Follows the three phases of the Sample-Guided Exact Top-K paper
+// (arXiv 2609.08450, Sec. 4), re-mapped onto CDNA4:
+//
+//  k_ragged_scan    one workgroup per (row, segment).  Phase 1: every segment
+//                   rebuilds the same block-strided view of its row (Sec. 4.2
+//                   and the KV-split mapping of Sec. 5.5), histograms the
+//                   11-bit coarse key in LDS, locates the primary and
+//                   secondary boundaries tau0/tau1 and turns them into
+//                   inclusive fp32 endpoints (Sec. 5.2).  Phase 2: one pass
+//                   over the segment with 16-byte non-temporal loads compares
+//                   each value with the endpoints (Sec. 5.3); admitted values
+//                   are appended to a per-wave slice whose slots come from a
+//                   ballot + popcount + lane-rank (no atomics), and the
+//                   secondary count is accumulated from a second ballot.
+//  k_ragged_finish  one workgroup per row.  Sums the per-wave counts and
+//                   picks the route: certified primary, band pass (Sec. 4.3
+//                   "Underfilled views"), or the exact route over the whole
+//                   row (Table 2).  Then exact_select refines the frontier
+//                   (Sec. 5.4) and writes the indices.
+//
+// The view samples 16 consecutive elements (one 64-byte segment) out of every
+// 16*s: 1/s of the row like a single-element stride, but every sampled byte
+// shares a cache line with its neighbours instead of pulling a whole line for
+// one float.
+#include "itk_device.hpp"
+#include "itk_internal.hpp"
+
+namespace itk {
+
+struct RaggedArgs {
+    const float *scores;
+    const int32_t *row_len;
+    int32_t *out_idx;
+    int32_t *route;
+    uint32_t *cnt;   // [M][P][W] admitted per (segment, wave); may exceed subcap
+    uint32_t *c1;    // [M][P][W] values >= secondary endpoint
+    float4 *ep;      // [M] {e0, e1, admit_all, 0}
+    Cand *slices;    // [M][P][W][subcap]
+    Cand *band;      // [M][bandcap]
+    int64_t pitch, seg;
+    int32_t M, k, P, subcap, bandcap, view_blocks, force;
+    float rho, rho1;
+};
+
+__device__ __forceinline__ uint32_t row_length(const RaggedArgs &a, int r)
+{
+    int32_t L = a.row_len[r];
+    if (L < 0) L = 0;
+    if ((int64_t)L > a.pitch) L = (int32_t)a.pitch;
+    return (uint32_t)L;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
+{
+    __shared__ uint32_t hist[NBINS];
+    __shared__ uint32_t scan_tmp[16];
+    __shared__ BoundaryOut b0, b1;
+    __shared__ float s_e[2];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = blockIdx.x / a.P, p = blockIdx.x % a.P;
+    const uint32_t L = row_length(a, r);
+    const int64_t seg_lo = (int64_t)p * a.seg;
+    const int64_t seg_hi = (seg_lo + a.seg < (int64_t)L) ? seg_lo + a.seg : (int64_t)L;
+    const size_t cell = ((size_t)r * a.P + p) * RAG_WAVES + wave;
+
+    if ((seg_lo >= (int64_t)L && p != 0) || a.force == 1) {
+        if (a.force == 1 && p == 0 && tid == 0) a.ep[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lane == 0) { a.cnt[cell] = 0u; a.c1[cell] = 0u; }
+        return;
+    }
+    const float *row = a.scores + (size_t)r * (size_t)a.pitch;
+
+    // ---- Phase 1: block-strided view -> coarse histogram -> endpoints.
+    for (int i = tid; i < NBINS; i += RAG_THREADS) hist[i] = 0u;
+    __syncthreads();
+    const uint32_t sb = (uint32_t)a.view_blocks;
+    const uint32_t phase = (uint32_t)r % sb;
+    const uint32_t nb_total = (L + 15u) >> 4;
+    const uint32_t nvb = nb_total > phase ? (nb_total - 1u - phase) / sb + 1u : 0u;
+    for (uint32_t e = tid; e < nvb * 16u; e += RAG_THREADS) {
+        const uint32_t i = (phase + (e >> 4) * sb) * 16u + (e & 15u);
+        if (i < L) atomicAdd(&hist[coarse_key(row[i])], 1u);
+    }
+    __syncthreads();
+    uint32_t n_a = 0;
+    if (nvb) {
+        const uint32_t last = (phase + (nvb - 1u) * sb) * 16u;
+        n_a = (nvb - 1u) * 16u + ((L - last) < 16u ? (L - last) : 16u);
+    }
+    const double frac = L ? (double)n_a / (double)L : 0.0;
+    const uint32_t q0 = (uint32_t)ceil((double)a.rho * a.k * frac);
+    const uint32_t q1 = (uint32_t)ceil((double)a.rho1 * a.k * frac);
+    const bool admit_all = (n_a < q1) || q0 == 0u || ((double)a.rho1 * a.k >= (double)L);
+    if (!admit_all) {
+        find_boundary<RAG_THREADS>(hist, q0, scan_tmp, &b0);
+        find_boundary<RAG_THREADS>(hist, q1, scan_tmp, &b1);
+    }
+    if (tid == 0) {
+        s_e[0] = admit_all ? -__builtin_inff() : coarse_endpoint(b0.digit);
+        s_e[1] = admit_all ? -__builtin_inff() : coarse_endpoint(b1.digit);
+        if (p == 0) a.ep[r] = make_float4(s_e[0], s_e[1], admit_all ? 1.f : 0.f, 0.f);
+    }
+    __syncthreads();
+    const float e0 = s_e[0], e1 = s_e[1];
+
+    // ---- Phase 2: certify + collect over [seg_lo, seg_hi).
+    Cand *slice = a.slices + cell * (size_t)a.subcap;
+    const uint32_t subcap = (uint32_t)a.subcap;
+    uint32_t cnt = 0, c1 = 0;  // wave-uniform
+    auto classify = [&](bool valid, uint32_t i, float x) {
+        const bool in1 = valid && x >= e1;
+        const bool in0 = valid && x >= e0;
+        c1 += (uint32_t)__popcll(__ballot(in1));
+        const uint64_t m0 = __ballot(in0);
+        const uint32_t slot = cnt + lanes_below(m0);
+        if (in0 && slot < subcap) slice[slot] = Cand{i, x};
+        cnt += (uint32_t)__popcll(m0);
+    };
+    if (seg_hi > seg_lo) {
+        if (VEC) {
+            constexpr int U = 4;
+            const uint32_t n4 = (uint32_t)((seg_hi - seg_lo) >> 2);
+            const f32x4_t *v4 = reinterpret_cast<const f32x4_t *>(row + seg_lo);
+            for (uint32_t base = 0; base < n4; base += RAG_THREADS * U) {
+                f32x4_t x[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t j = base + u * RAG_THREADS + tid;
+                    x[u] = j < n4 ? __builtin_nontemporal_load(v4 + j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t j = base + u * RAG_THREADS + tid;
+                    const bool valid = j < n4;
+                    const uint32_t i0 = (uint32_t)seg_lo + 4u * j;
+                    classify(valid, i0 + 0u, x[u].x);
+                    classify(valid, i0 + 1u, x[u].y);
+                    classify(valid, i0 + 2u, x[u].z);
+                    classify(valid, i0 + 3u, x[u].w);
+                }
+            }
+            const uint32_t rem_lo = (uint32_t)seg_lo + 4u * n4;
+            if (wave == 0 && rem_lo < (uint32_t)seg_hi) {
+                const uint32_t i = rem_lo + lane;
+                const bool valid = i < (uint32_t)seg_hi;
+                classify(valid, i, valid ? row[i] : 0.f);
+            }
+        } else {
+            for (int64_t base = seg_lo; base < seg_hi; base += RAG_THREADS) {
+                const int64_t i = base + tid;
+                const bool valid = i < seg_hi;
+                classify(valid, (uint32_t)i, valid ? row[i] : 0.f);
+            }
+        }
+    }
+    if (lane == 0) {
+        a.cnt[cell] = cnt;
+        a.c1[cell] = c1;
+    }
+}
+
+// Items of a row's candidate slices (and band slice), for exact_select.
+struct SliceSrc {
+    const Cand *slices;     // [ncells][subcap]
+    const uint32_t *cnt;    // [ncells]
+    int ncells;
+    uint32_t subcap;
+    const Cand *band;
+    uint32_t band_n;
+    template <class F>
+    __device__ void for_each(F &&f) const
+    {
+        for (int c = 0; c < ncells; ++c) {
+            const uint32_t n = cnt[c] < subcap ? cnt[c] : subcap;
+            const Cand *s = slices + (size_t)c * subcap;
+            for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+                const Cand e = s[i];
+                f(e.idx, e.val);
+            }
+        }
+        for (uint32_t i = threadIdx.x; i < band_n; i += blockDim.x) {
+            const Cand e = band[i];
+            f(e.idx, e.val);
+        }
+    }
+};
+
+// Every valid entry of one row.
+struct RowSrc {
+    const float *row;
+    uint32_t L;
+    bool vec;
+    template <class F>
+    __device__ void for_each(F &&f) const
+    {
+        if (vec) {
+            const uint32_t n4 = L >> 2;
+            const float4 *v4 = reinterpret_cast<const float4 *>(row);
+            for (uint32_t j = threadIdx.x; j < n4; j += blockDim.x) {
+                const float4 x = v4[j];
+                f(4u * j + 0u, x.x);
+                f(4u * j + 1u, x.y);
+                f(4u * j + 2u, x.z);
+                f(4u * j + 3u, x.w);
+            }
+            for (uint32_t i = 4u * n4 + threadIdx.x; i < L; i += blockDim.x) f(i, row[i]);
+        } else {
+            for (uint32_t i = threadIdx.x; i < L; i += blockDim.x) f(i, row[i]);
+        }
+    }
+};
+
+enum { ROUTE_SAMPLE = 1, ROUTE_BAND = 2, ROUTE_EXACT = 3, ROUTE_ALL = 4 };
+
+__global__ __launch_bounds__(RAG_THREADS) void k_ragged_finish(RaggedArgs a, int vec)
+{
+    __shared__ SelectSmem sm;
+    __shared__ uint32_t s_c0, s_c1, s_ovf, s_band_n;
+    __shared__ int s_route;
+
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x;
+    const uint32_t L = row_length(a, r);
+    const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+    int32_t *out = a.out_idx + (size_t)r * a.k;
+    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += RAG_THREADS) out[i] = -1;
+    if (need == 0) {
+        if (tid == 0 && a.route) a.route[r] = ROUTE_ALL;
+        return;
+    }
+    if (tid == 0) { s_c0 = 0; s_c1 = 0; s_ovf = 0; s_band_n = 0; }
+    __syncthreads();
+    const int ncells = a.P * RAG_WAVES;
+    const size_t cell0 = (size_t)r * ncells;
+    for (int c = tid; c < ncells; c += RAG_THREADS) {
+        const uint32_t n = a.cnt[cell0 + c];
+        atomicAdd(&s_c0, n);
+        atomicAdd(&s_c1, a.c1[cell0 + c]);
+        if (n > (uint32_t)a.subcap) atomicOr(&s_ovf, 1u);
+    }
+    __syncthreads();
+    const float4 ep = a.ep[r];
+    const float *row = a.scores + (size_t)r * (size_t)a.pitch;
+    if (tid == 0) {
+        const uint32_t C0 = s_c0, C1 = s_c1;
+        int route = ROUTE_EXACT;
+        if (a.force == 1 || s_ovf) route = ROUTE_EXACT;
+        else if (C0 >= need && a.force != 2) route = ep.z != 0.f ? ROUTE_ALL : ROUTE_SAMPLE;
+        else if (C1 >= need && C1 - C0 <= (uint32_t)a.bandcap) route = ROUTE_BAND;
+        s_route = route;
+    }
+    __syncthreads();
+    const int route = s_route;
+
+    if (route == ROUTE_BAND) {
+        // Second traversal: append the values admitted by the secondary
+        // endpoint but not by the primary one.
+        Cand *band = a.band + (size_t)r * a.bandcap;
+        const float e0 = ep.x, e1 = ep.y;
+        RowSrc rs{row, L, vec != 0};
+        rs.for_each([&](uint32_t i, float x) {
+            const bool in = x >= e1 && !(x >= e0);
+            const uint32_t slot = wave_reserve(in, &s_band_n);
+            if (in && slot < (uint32_t)a.bandcap) band[slot] = Cand{i, x};
+        });
+        __syncthreads();
+    }
+
+    auto emit = [&](uint32_t slot, uint64_t K) {
+        if (slot < need) out[slot] = (int32_t)key_index(K);
+    };
+    if (route == ROUTE_EXACT) {
+        RowSrc src{row, L, vec != 0};
+        exact_select<RAG_THREADS>(sm, src, need, emit);
+    } else {
+        SliceSrc src{a.slices + cell0 * (size_t)a.subcap, a.cnt + cell0, ncells, (uint32_t)a.subcap,
+                     a.band + (size_t)r * a.bandcap, route == ROUTE_BAND ? s_band_n : 0u};
+        exact_select<RAG_THREADS>(sm, src, need, emit);
+    }
+    if (tid == 0 && a.route) a.route[r] = route;
+}
+
+static int ceil_div_i(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
+{
+    const Knobs &kn = knobs();
+    RaggedPlan p;
+    p.M = M; p.pitch = pitch; p.k = k;
+    int target = ceil_div_i(512, M);
+    if (target < 1) target = 1;
+    if (target > 16) target = 16;
+    if (kn.splits > 0) target = kn.splits;
+    int64_t seg = (pitch + target - 1) / target;
+    seg = ((seg + 1023) / 1024) * 1024;
+    if (seg < 4096) seg = 4096;
+    p.seg = seg;
+    p.P = ceil_div_i(pitch > 0 ? pitch : 1, seg);
+    int s = pitch >= 262144 ? 128 : 64;
+    if (kn.sample_stride > 0) s = kn.sample_stride;
+    p.view_blocks = s;
+    p.rho = kn.rho > 0.f ? kn.rho : 1.5f;
+    p.rho1 = kn.rho1 > 0.f ? kn.rho1 : 1.75f;
+    if (p.rho1 < p.rho) p.rho1 = p.rho;
+    int segcap = (int)(2.0 * p.rho1 * k + 0.5);
+    if (segcap < 2048) segcap = 2048;
+    if (kn.capacity > 0) segcap = kn.capacity;
+    p.subcap = (segcap + RAG_WAVES - 1) / RAG_WAVES;
+    p.subcap = (p.subcap + 63) & ~63;
+    p.bandcap = 2 * k > 2048 ? 2 * k : 2048;
+    p.force = kn.force_route;
+    const size_t cells = (size_t)M * p.P * RAG_WAVES;
+    size_t off = 0;
+    p.off_cnt = off; off = align256(off + cells * 4);
+    p.off_c1 = off; off = align256(off + cells * 4);
+    p.off_ep = off; off = align256(off + (size_t)M * 16);
+    p.off_slices = off; off = align256(off + cells * (size_t)p.subcap * sizeof(Cand));
+    p.off_band = off; off = align256(off + (size_t)M * p.bandcap * sizeof(Cand));
+    p.bytes = off;
+    return p;
+}
+
+hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t *row_len, int32_t *out_idx,
+                         void *ws, hipStream_t stream)
+{
+    char *w = static_cast<char *>(ws);
+    RaggedArgs a;
+    a.scores = scores;
+    a.row_len = row_len;
+    a.out_idx = out_idx;
+    const RouteSink &rs = route_sink();
+    a.route = (rs.ptr && rs.rows >= p.M) ? rs.ptr : nullptr;
+    a.cnt = reinterpret_cast<uint32_t *>(w + p.off_cnt);
+    a.c1 = reinterpret_cast<uint32_t *>(w + p.off_c1);
+    a.ep = reinterpret_cast<float4 *>(w + p.off_ep);
+    a.slices = reinterpret_cast<Cand *>(w + p.off_slices);
+    a.band = reinterpret_cast<Cand *>(w + p.off_band);
+    a.pitch = p.pitch;
+    a.seg = p.seg;
+    a.M = p.M; a.k = p.k; a.P = p.P; a.subcap = p.subcap; a.bandcap = p.bandcap;
+    a.view_blocks = p.view_blocks; a.force = p.force;
+    a.rho = p.rho; a.rho1 = p.rho1;
+    const bool vec = (p.pitch % 4 == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0);
+    {
+        StageTimer st(ST_RAG_SCAN, stream);
+        if (vec) hipLaunchKernelGGL(k_ragged_scan<true>, dim3(p.M * p.P), dim3(RAG_THREADS), 0, stream, a);
+        else hipLaunchKernelGGL(k_ragged_scan<false>, dim3(p.M * p.P), dim3(RAG_THREADS), 0, stream, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    {
+        StageTimer st(ST_RAG_FINISH, stream);
+        hipLaunchKernelGGL(k_ragged_finish, dim3(p.M), dim3(RAG_THREADS), 0, stream, a, vec ? 1 : 0);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace itk

@@ -1,0 +1,68 @@
+"""Acceptance checks of HIP results against the CPU oracle (test helpers).
+
+Fused path (scores differ from the oracle only by fp32 accumulation order):
+  (i)   every returned score is within tol of the oracle score of its index,
+        relative to max(|oracle score|, |oracle k-th score|);
+  (ii)  every returned index's oracle score >= oracle k-th score - tol*|k-th|;
+  (iii) |out| = min(k, L), indices distinct and in [0, L), padding -1 / -inf;
+  (iv)  recall |S_gpu & S_oracle| / min(k, L) is reported.
+Standalone path: the index sets are bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+TOL = {0: 2e-2, 1: 2e-2, 2: 2e-2, 3: 6e-2}  # by key dtype: f32, bf16, f16, fp8
+
+
+def check_fused_rows(case, rows, gpu_idx, gpu_score, tol=None, min_recall=None):
+    """Check rows ``rows`` of a fused result; returns the per-row recalls."""
+    tol = TOL[case.k_dtype] if tol is None else tol
+    rows = np.asarray(rows, dtype=np.int32)
+    o_idx, o_val, o_n = oracle.fused_topk(case, rows=rows)
+    recalls = []
+    for r, t in enumerate(rows):
+        L = int(case.kv_len[t])
+        need = min(case.k, max(L, 0))
+        gi = np.asarray(gpu_idx[t])
+        gs = np.asarray(gpu_score[t])
+        assert o_n[r] == need
+        assert (gi[need:] == -1).all(), f"row {t}: padding indices"
+        assert np.isneginf(gs[need:]).all(), f"row {t}: padding scores"
+        sel = gi[:need]
+        assert len(np.unique(sel)) == need, f"row {t}: duplicate indices"
+        assert ((sel >= 0) & (sel < L)).all(), f"row {t}: index out of range"
+        if need == 0:
+            recalls.append(1.0)
+            continue
+        kth = o_val[r, need - 1]
+        ora_sel = oracle.fused_scores_at(case, np.full(need, t), sel)
+        denom = np.maximum(np.abs(ora_sel), abs(kth))
+        denom = np.where(denom > 0, denom, 1.0)
+        err = np.abs(gs[:need].astype(np.float64) - ora_sel) / denom
+        assert err.max() <= tol, f"row {t}: score error {err.max():.3g} > {tol}"
+        assert (ora_sel >= kth - tol * abs(kth)).all(), \
+            f"row {t}: selected score {ora_sel.min():.6g} below k-th {kth:.6g}"
+        rec = len(set(sel.tolist()) & set(o_idx[r, :need].tolist())) / need
+        recalls.append(rec)
+    recalls = np.asarray(recalls)
+    if min_recall is not None:
+        assert recalls.min() >= min_recall, f"recall {recalls.min():.4f} < {min_recall}"
+    return recalls
+
+
+def check_ragged_exact(case, gpu_idx, rows=None):
+    rows = np.arange(case.M) if rows is None else np.asarray(rows)
+    o_idx, o_n = oracle.topk_ragged(case, rows=rows)
+    for r, m in enumerate(rows):
+        need = int(o_n[r])
+        gi = np.asarray(gpu_idx[m])
+        assert (gi[need:] == -1).all(), f"row {m}: padding"
+        got = np.sort(gi[:need])
+        exp = np.sort(o_idx[r, :need])
+        if not np.array_equal(got, exp):
+            miss = np.setdiff1d(exp, got)[:8]
+            extra = np.setdiff1d(got, exp)[:8]
+            raise AssertionError(f"row {m} (L={case.row_len[m]}): missing {miss.tolist()} extra {extra.tolist()}")

@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every declared symbol, and validates its
+arguments on the host (no GPU needed: invalid calls return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import indexer_exact_top_amd as itk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "itk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)
+    return sorted({n for n in names if n.startswith(("itk_", "topk_", "indexer_"))})
+
+
+def test_every_declared_symbol_is_exported():
+    lib = itk.lib()
+    names = _declared_functions()
+    assert "indexer_topk_fused" in names and "topk_ragged" in names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+
+
+def test_status_strings():
+    lib = itk.lib()
+    assert lib.itk_status_string(0) == b"ok"
+    assert lib.itk_status_string(3).startswith(b"workspace")
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)  # never dereferenced: validation fails first
+
+
+def test_ragged_validation():
+    lib = itk.lib()
+    ws = lib.topk_ragged_workspace_size(64, 131072, 2048)
+    assert ws > 0
+    assert lib.topk_ragged(None, 128, FAKE, 4, 8, FAKE, FAKE, ws, None) == 1
+    assert lib.topk_ragged(FAKE, 128, FAKE, 0, 8, FAKE, FAKE, ws, None) == 1
+    assert lib.topk_ragged(FAKE, 128, FAKE, 4, 0, FAKE, FAKE, ws, None) == 1
+    assert lib.topk_ragged(FAKE, 0, FAKE, 4, 8, FAKE, FAKE, ws, None) == 1
+    assert lib.topk_ragged(FAKE, 1 << 31, FAKE, 4, 8, FAKE, FAKE, ws, None) == 2
+    need = lib.topk_ragged_workspace_size(4, 128, 8)
+    assert lib.topk_ragged(FAKE, 128, FAKE, 4, 8, FAKE, None, need, None) == 3
+    assert lib.topk_ragged(FAKE, 128, FAKE, 4, 8, FAKE, FAKE, need - 1, None) == 3
+    assert lib.topk_ragged(FAKE, 128, FAKE, 4, 8, FAKE, P(0x10010), need, None) == 3  # misaligned
+
+
+def test_fused_validation():
+    lib = itk.lib()
+    BF, F16, F32, FP8 = itk.BF16, itk.F16, itk.F32, itk.FP8_E4M3
+    args = lambda **kw: dict(dict(Q=FAKE, qt=BF, K=FAKE, kt=BF, S=None, W=FAKE, kv=FAKE, T=4, H=8, D=64, N=1000,
+                                  k=16, flags=0, oi=FAKE, os=FAKE, ws=FAKE, wsb=1 << 40), **kw)
+
+    def call(a):
+        return lib.indexer_topk_fused(a["Q"], a["qt"], a["K"], a["kt"], a["S"], a["W"], a["kv"], a["T"], a["H"],
+                                      a["D"], a["N"], a["k"], a["flags"], a["oi"], a["os"], a["ws"], a["wsb"], None)
+
+    assert call(args(Q=None)) == 1
+    assert call(args(kt=FP8)) == 1                  # fp8 keys need a scale
+    assert call(args(S=FAKE)) == 1                  # a scale only with fp8 keys
+    assert call(args(T=0)) == 1
+    assert call(args(k=0)) == 1
+    assert call(args(H=65)) == 2
+    assert call(args(D=96)) == 2
+    assert call(args(H=40, D=256)) == 2             # two head blocks need D <= 128
+    assert call(args(qt=F32, kt=BF)) == 2           # unsupported pair
+    assert call(args(qt=F32, kt=F32, H=40, D=128)) == 2
+    assert call(args(flags=1, H=2)) == 1            # NO_RELU needs H == 1
+    assert call(args(flags=4)) == 1
+    assert call(args(Q=P(0x10004))) == 1            # misaligned
+    assert call(args(ws=None)) == 3
+    assert call(args(wsb=16)) == 3
+
+
+def test_fused_workspace_is_O_rows_k():
+    lib = itk.lib()
+    f = lambda T, N, k, H=64, D=128, qt=itk.BF16, kt=itk.BF16, fl=0: \
+        lib.indexer_topk_fused_workspace_size(T, H, D, N, k, qt, kt, fl)
+    # config 3 / 4 / 5 against their materialized fp32 score matrices
+    c3 = f(2048, 133120, 2048)
+    c4 = f(128, 1 << 20, 2048, kt=itk.FP8_E4M3)
+    c5 = f(1024, 1 << 22, 4096, H=1, D=256, qt=itk.F16, kt=itk.F16, fl=1)
+    assert 0 < c3 < 2048 * 133120 * 4 / 4
+    assert 0 < c4 < 128 * (1 << 20) * 4 / 16
+    assert 0 < c5 < 1024 * (1 << 22) * 4 / 32
+    # independent of the key count, linear in rows and k
+    assert f(2048, 1 << 20, 2048) == pytest.approx(c3, rel=0.01)
+    assert f(4096, 133120, 2048) == pytest.approx(2 * c3, rel=0.02)
+    assert f(2048, 133120, 4096) < 2.1 * c3
+
+
+def test_materialized_baseline_arithmetic():
+    # The pages' materialization figures, which the O(rows*k) scratch avoids:
+    # LiteTopK Sec. 1: an 8192-query chunk over 2^20 keys in fp32 is 32 GB.
+    assert 8192 * (1 << 20) * 4 == 32 * (1 << 30)
+    # StreamIndex abstract: [B=1, S=65536, H_I=64, T=S/4] fp32 is 256 GB.
+    assert 1 * 65536 * 64 * (65536 // 4) * 4 == 256 * (1 << 30)
+
+
+def test_plan_opts_validation():
+    lib = itk.lib()
+    bad = itk.PlanOpts(-1, 0, 0, 0, 0, 0)
+    assert lib.itk_set_plan_opts(ctypes.byref(bad)) == 1
+    bad = itk.PlanOpts(0, 0, 0, 0, 0, 3)
+    assert lib.itk_set_plan_opts(ctypes.byref(bad)) == 1
+    ok = itk.PlanOpts(0, 0, 0, 512, 0, 0)
+    assert lib.itk_set_plan_opts(ctypes.byref(ok)) == 0
+    small = lib.topk_ragged_workspace_size(64, 131072, 2048)
+    assert lib.itk_set_plan_opts(None) == 0
+    assert lib.topk_ragged_workspace_size(64, 131072, 2048) > small

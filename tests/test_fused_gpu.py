@@ -1,0 +1,105 @@
+"""indexer_topk_fused on the GPU against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import check_fused_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _reset(itk):
+    itk.reset_plan_opts()
+    yield
+    itk.reset_plan_opts()
+
+
+def _run(itk, case, routes=False):
+    Q, K, S, W, kv = itk.fused_tensors(case)
+    rb = None
+    if routes:
+        rb = torch.zeros(case.T, dtype=torch.int32, device="cuda")
+        itk.set_route_buffer(rb)
+    try:
+        idx, sc = itk.indexer_topk_fused(Q, K, W, kv, case.k, k_scale=S, flags=case.flags)
+        torch.cuda.synchronize()
+    finally:
+        if routes:
+            itk.set_route_buffer(None)
+    return idx.cpu().numpy(), sc.cpu().numpy(), (rb.cpu().numpy() if routes else None)
+
+
+def test_config1_all_rows(itk):
+    case = synth.fused_config(1)
+    idx, sc, routes = _run(itk, case, routes=True)
+    rec = check_fused_rows(case, range(case.T), idx, sc, min_recall=0.99)
+    print(f"config1 recall mean {rec.mean():.4f} min {rec.min():.4f}; routes", np.bincount(routes).tolist())
+
+
+@pytest.mark.parametrize("qt,kt,H,D", [
+    (synth.BF16, synth.BF16, 64, 128), (synth.BF16, synth.BF16, 8, 64), (synth.BF16, synth.BF16, 33, 64),
+    (synth.BF16, synth.FP8_E4M3, 64, 128), (synth.F16, synth.F16, 16, 256), (synth.F16, synth.FP8_E4M3, 32, 128),
+    (synth.F32, synth.F32, 8, 128), (synth.F32, synth.F32, 40, 64),
+])
+def test_dtype_shapes(itk, qt, kt, H, D):
+    T, N, k = 19, 9000, 300
+    kv = np.array([9000, 8999, 8000, 301, 300, 299, 1, 0, 64, 65, 4500] + [9000 - 37 * i for i in range(8)],
+                  dtype=np.int32)
+    case = synth.gen_fused(T, H, D, N, k, q_dtype=qt, k_dtype=kt, kv_len=kv, seed=H * 7 + D)
+    idx, sc, _ = _run(itk, case)
+    check_fused_rows(case, range(T), idx, sc, min_recall=0.95)
+
+
+def test_inner_product_single_head(itk):
+    case = synth.gen_fused(12, 1, 256, 20000, 500, q_dtype=synth.F16, k_dtype=synth.F16, no_relu=True,
+                           unit_norm=True, seed=5)
+    idx, sc, _ = _run(itk, case)
+    check_fused_rows(case, range(case.T), idx, sc, min_recall=0.95)
+
+
+def test_relu_zero_rows_recover_exactly(itk):
+    # Negative queries against positive keys: every score is exactly 0, so the
+    # answer is the k lowest indices and the row must take the recovery route.
+    T, H, D, N, k = 9, 8, 64, 5000, 100
+    rng = np.random.default_rng(0)
+    q = -np.abs(rng.standard_normal((T, H, D))).astype(np.float32)
+    kk = np.abs(rng.standard_normal((N, D))).astype(np.float32)
+    case = synth.FusedCase(name="zero", T=T, H=H, D=D, N=N, k=k, q_dtype=synth.BF16, k_dtype=synth.BF16,
+                           q_bits=synth.encode(q, synth.BF16), k_bits=synth.encode(kk, synth.BF16), k_scale=None,
+                           W=rng.random((T, H)).astype(np.float32), kv_len=np.full(T, N, np.int32))
+    idx, sc, routes = _run(itk, case, routes=True)
+    for t in range(T):
+        assert sorted(idx[t].tolist()) == list(range(k))
+        assert (sc[t] == 0).all()
+    print("zero-row routes", routes.tolist())
+
+
+@pytest.mark.parametrize("knobs", [dict(force_route=1), dict(capacity=2048, rho=50.0), dict(splits=8),
+                                   dict(sample_stride=1, rho=1.0), dict(splits=3, sample_stride=5)])
+def test_routes_and_plans_give_identical_sets(itk, knobs):
+    case = synth.gen_fused(16, 64, 128, 40000, 512, q_dtype=synth.BF16, k_dtype=synth.BF16,
+                           kv_len=np.arange(16) * 1000 + 25000, seed=44)
+    base, bsc, _ = _run(itk, case)
+    itk.set_plan_opts(**knobs)
+    got, gsc, routes = _run(itk, case, routes=True)
+    print(knobs, "routes", np.bincount(routes).tolist())
+    check_fused_rows(case, range(case.T), got, gsc, min_recall=0.95)
+    # the kernel's own fp32 scores are route-independent, so the sets match exactly
+    assert np.array_equal(np.sort(base, axis=1), np.sort(got, axis=1))
+
+
+def test_config3_sampled_rows(itk):
+    case = synth.fused_config(3, T=64)
+    idx, sc, routes = _run(itk, case, routes=True)
+    rows = [0, 17, 40, 63]
+    rec = check_fused_rows(case, rows, idx, sc, min_recall=0.99)
+    print(f"config3 (T=64) recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
+
+
+def test_config4_sampled_rows(itk):
+    case = synth.fused_config(4, T=16)
+    idx, sc, routes = _run(itk, case, routes=True)
+    rec = check_fused_rows(case, [0, 9], idx, sc, min_recall=0.95)
+    print(f"config4 (T=16) recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
