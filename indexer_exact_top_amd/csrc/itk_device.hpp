@@ -75,13 +75,15 @@ __device__ __forceinline__ uint32_t coarse_key(float x)
 }
 
 // Smallest fp32 value x (over [-inf, +inf]) with coarse_key(x) >= tau: then
-// "x >= endpoint" reproduces "coarse_key(x) >= tau" with one compare.
+// "x >= endpoint" reproduces "coarse_key(x) >= tau" with one compare.  Bins
+// above the bin of +inf hold only NaN codes; their endpoint is NaN, which
+// admits no value.
 __device__ inline float coarse_endpoint(uint32_t tau)
 {
     uint32_t lo = ordered_key(-__builtin_inff());
     uint32_t hi = ordered_key(__builtin_inff());
     if (coarse_key(from_ordered_key(lo)) >= tau) return -__builtin_inff();
-    if (coarse_key(from_ordered_key(hi)) < tau) return __builtin_inff();
+    if (coarse_key(from_ordered_key(hi)) < tau) return __builtin_nanf("");
     while (hi - lo > 1u) {  // coarse(lo) < tau <= coarse(hi)
         const uint32_t mid = lo + ((hi - lo) >> 1);
         if (coarse_key(from_ordered_key(mid)) >= tau) hi = mid;
