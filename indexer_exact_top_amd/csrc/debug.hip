@@ -15,12 +15,18 @@ __global__ void k_debug_mfma(const typename MTraits<MT>::frag *a, const typename
     for (int r = 0; r < 16; ++r) c[l * 16 + r] = acc[r];
 }
 
+// Widens codes 4 at a time, as the key staging does (a partial last group
+// is padded with zero codes, which are not stored).
 __global__ void k_debug_fp8(const uint8_t *in, uint16_t *bf, uint16_t *hf, int n)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) {
-        bf[i] = (uint16_t)fp8_to_bf16_bits(in[i]);
-        hf[i] = (uint16_t)fp8_to_f16_bits(in[i]);
+    const int i0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+    if (i0 >= n) return;
+    uint32_t word = 0;
+    for (int j = 0; j < 4 && i0 + j < n; ++j) word |= (uint32_t)in[i0 + j] << (8 * j);
+    const u32x2_t b = fp8x4_widen<M_BF16>(word), h = fp8x4_widen<M_F16>(word);
+    for (int j = 0; j < 4 && i0 + j < n; ++j) {
+        bf[i0 + j] = (uint16_t)(b[j >> 1] >> (16 * (j & 1)));
+        hf[i0 + j] = (uint16_t)(h[j >> 1] >> (16 * (j & 1)));
     }
 }
 
@@ -60,7 +66,7 @@ itk_status itk_debug_mfma(int32_t mtype, const void *a_frags, const void *b_frag
 itk_status itk_debug_fp8(const uint8_t *in, uint16_t *bf16_out, uint16_t *f16_out, int32_t n, void *stream)
 {
     if (!in || !bf16_out || !f16_out || n <= 0) return ITK_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(k_debug_fp8, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), in,
+    hipLaunchKernelGGL(k_debug_fp8, dim3((n + 1023) / 1024), dim3(256), 0, static_cast<hipStream_t>(stream), in,
                        bf16_out, f16_out, n);
     return hipGetLastError() == hipSuccess ? ITK_OK : ITK_ERR_HIP;
 }

@@ -80,20 +80,20 @@ __device__ __forceinline__ f32x16_t mfma32(typename MTraits<MT>::frag a, typenam
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// e4m3fn byte -> bf16 / fp16 bits (exact; both formats hold every e4m3fn value).
-__device__ __forceinline__ uint32_t fp8_to_bf16_bits(uint32_t b)
+// Four e4m3fn codes (the bytes of `word`, lowest first) -> four bf16 or fp16
+// values, two per dword, lowest first.  Uses the gfx950 scaled conversion
+// with a unit scale; both 16-bit formats hold every e4m3fn value exactly.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <int MT>
+__device__ __forceinline__ u32x2_t fp8x4_widen(uint32_t word)
 {
-    const uint32_t s = (b & 0x80u) << 8, e = (b >> 3) & 15u, m = b & 7u;
-    if (e == 15u && m == 7u) return s | 0x7FC0u;
-    if (e == 0u) return s | (__float_as_uint((float)m * 0x1p-9f) >> 16);
-    return s | ((e + 120u) << 7) | (m << 4);
-}
-__device__ __forceinline__ uint32_t fp8_to_f16_bits(uint32_t b)
-{
-    const uint32_t s = (b & 0x80u) << 8, e = (b >> 3) & 15u, m = b & 7u;
-    if (e == 15u && m == 7u) return s | 0x7E00u;
-    if (e == 0u) return s | (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)((float)m * 0x1p-9f));
-    return s | ((e + 8u) << 10) | (m << 7);
+    if constexpr (MT == M_BF16)
+        return u32x2_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true))};
+    else
+        return u32x2_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true))};
 }
 
 // Kernel configuration: Q dtype, K dtype, head blocks, head dim, ReLU.
@@ -206,71 +206,115 @@ struct QFrags {
             }
         }
     }
-};
 
-// Register epilogue: per lane, sum over its head rows of w * ReLU(acc), then
-// combine the two half-waves so that lane l holds the score of key column
-// l of block 0 (l < 32) or l - 32 of block 1 (l >= 32).
-template <class C>
-__device__ __forceinline__ float reduce_heads(const f32x16_t (&acc)[2][C::HB], const float (&w)[C::HB][16])
-{
-    float part[2];
+    // Make the loaded fragments resident before a loop that uses them.  The
+    // waits for these loads then sit here, once, instead of inside the loop
+    // where they would also wait for that loop's own prefetches.
+    __device__ __forceinline__ void settle()
+    {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        float s = 0.f;
+        for (int hb = 0; hb < C::HB; ++hb) {
 #pragma unroll
-        for (int hb = 0; hb < C::HB; ++hb)
+            for (int kk = 0; kk < C::KS; ++kk) asm volatile("" : "+v"(q[hb][kk]));
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x = acc[kb][hb][r];
-                s = fmaf(w[hb][r], C::RELU ? fmaxf(x, 0.f) : x, s);
-            }
-        part[kb] = s;
-    }
-    const bool lo = lane_id() < 32u;
-    const float other = __shfl_xor(lo ? part[1] : part[0], 32);
-    return (lo ? part[0] : part[1]) + other;
-}
-
-// Scores of 64 keys from a staged LDS tile: lane l gets key tile_start + l.
-template <class C>
-__device__ __forceinline__ float tile_scores_lds(const QFrags<C> &qf, const char *ktile)
-{
-    const int l = (int)lane_id();
-    f32x16_t acc[2][C::HB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hb = 0; hb < C::HB; ++hb) acc[kb][hb] = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const char *row = ktile + (kb * 32 + (l & 31)) * C::ROWB;
-            typename C::frag b;
-            if constexpr (C::MT == M_F32)
-                b = *reinterpret_cast<const float *>(row + (kk * 2 + (l >> 5)) * 4);
-            else
-                b = *reinterpret_cast<const u32x4_t *>(row + (kk * 16 + 8 * (l >> 5)) * 2);
-#pragma unroll
-            for (int hb = 0; hb < C::HB; ++hb) acc[kb][hb] = mfma32<C::MT>(qf.q[hb][kk], b, acc[kb][hb]);
+            for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(w[hb][r]));
         }
     }
-    return reduce_heads<C>(acc, qf.w);
+};
+
+// ReLU of an fp32 value as one integer max: negative values (sign bit set,
+// including -0) compare below 0 as int32 and become +0; positive values keep
+// their bits.  Unlike fmaxf it needs no NaN canonicalisation.
+__device__ __forceinline__ float relu_bits(float x)
+{
+    return __int_as_float(max(__float_as_int(x), 0));
 }
 
-// Same, with B fragments read straight from global K (recovery path).
+// Head reduction of one 32-key block: lane l sums w * ReLU(acc) over the 16
+// head rows it holds in each 32-head block, for key column l % 32.  The two
+// half-waves hold disjoint head rows of the same keys.
+template <class C>
+__device__ __forceinline__ float reduce_block(const f32x16_t (&acc)[C::HB], const float (&w)[C::HB][16])
+{
+    float s = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < C::HB; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float x = acc[hb][r];
+            s = fmaf(w[hb][r], C::RELU ? relu_bits(x) : x, s);
+        }
+    return s;
+}
+
+// Combine the half-wave partials of two consecutive 32-key blocks so that
+// lane l holds the score of key l of the 64-key tile: v_permlane32_swap
+// exchanges the upper half of p0 with the lower half of p1, after which
+// lane l < 32 holds p0[l] and p0[l + 32] and lane l >= 32 holds p1[l - 32]
+// and p1[l].
+__device__ __forceinline__ float combine_halves(float p0, float p1)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// B fragments of one 32-key block (kb) of a staged tile: lane l supplies key
+// column kb * 32 + l % 32 at the k-slice selected by l / 32.
+template <class C>
+__device__ __forceinline__ void load_bfrags(typename C::frag (&b)[C::KS], const char *ktile, int kb)
+{
+    const int l = (int)lane_id();
+    const char *row = ktile + (kb * 32 + (l & 31)) * C::ROWB;
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) {
+        if constexpr (C::MT == M_F32)
+            b[kk] = *reinterpret_cast<const float *>(row + (kk * 2 + (l >> 5)) * 4);
+        else
+            b[kk] = *reinterpret_cast<const u32x4_t *>(row + (kk * 16 + 8 * (l >> 5)) * 2);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_block(f32x16_t (&acc)[C::HB], const QFrags<C> &qf,
+                                           const typename C::frag (&b)[C::KS])
+{
+#pragma unroll
+    for (int hb = 0; hb < C::HB; ++hb) acc[hb] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb) acc[hb] = mfma32<C::MT>(qf.q[hb][kk], b[kk], acc[hb]);
+}
+
+// Scheduling hint for one block: the B-fragment LDS reads first, then every
+// MFMA followed by a few VALU instructions of the previous block's head
+// reduction, so that the reduction issues while the matrix core works.
+template <class C>
+__device__ __forceinline__ void sched_block()
+{
+    constexpr int NM = C::KS * C::HB;
+    constexpr int NV = 32 * C::HB;  // max + fma per accumulator register
+    constexpr int PER = (NV + NM - 1) / NM;
+#pragma unroll
+    for (int i = 0; i < C::KS; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+    }
+}
+
+// Same scores with B fragments read straight from global K (recovery path).
 template <class C>
 __device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int64_t key0)
 {
     const int l = (int)lane_id();
-    f32x16_t acc[2][C::HB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hb = 0; hb < C::HB; ++hb) acc[kb][hb] = f32x16_t{};
+    float part[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+        f32x16_t acc[C::HB];
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb) acc[hb] = f32x16_t{};
         const int64_t key = key0 + kb * 32 + (l & 31);
         const bool ok = key < a.N;
         const char *krow = static_cast<const char *>(a.K) + (size_t)(ok ? key : 0) * C::D * C::kbytes;
@@ -282,36 +326,38 @@ __device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int
             } else if constexpr (C::KT == ITK_FP8_E4M3) {
                 const int d0 = kk * 16 + 8 * (l >> 5);
                 const u32x2_t raw = ok ? *reinterpret_cast<const u32x2_t *>(krow + d0) : u32x2_t{0u, 0u};
-                u32x4_t v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t word = raw[e >> 1];
-                    const uint32_t b0 = (word >> (16 * (e & 1))) & 0xFFu, b1 = (word >> (16 * (e & 1) + 8)) & 0xFFu;
-                    const uint32_t h0 = C::MT == M_BF16 ? fp8_to_bf16_bits(b0) : fp8_to_f16_bits(b0);
-                    const uint32_t h1 = C::MT == M_BF16 ? fp8_to_bf16_bits(b1) : fp8_to_f16_bits(b1);
-                    v[e] = h0 | (h1 << 16);
-                }
-                b = v;
+                const u32x2_t lo = fp8x4_widen<C::MT>(raw[0]), hi = fp8x4_widen<C::MT>(raw[1]);
+                b = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
             } else {
                 const int d0 = kk * 16 + 8 * (l >> 5);
                 b = ok ? *reinterpret_cast<const u32x4_t *>(krow + d0 * 2) : u32x4_t{0u, 0u, 0u, 0u};
             }
 #pragma unroll
-            for (int hb = 0; hb < C::HB; ++hb) acc[kb][hb] = mfma32<C::MT>(qf.q[hb][kk], b, acc[kb][hb]);
+            for (int hb = 0; hb < C::HB; ++hb) acc[hb] = mfma32<C::MT>(qf.q[hb][kk], b, acc[hb]);
         }
+        part[kb] = reduce_block<C>(acc, qf.w);
     }
-    return reduce_heads<C>(acc, qf.w);
+    return combine_halves(part[0], part[1]);
 }
 
 // ---------------------------------------------------- tile staging (LDS)
+// Double-buffered key tiles (and the per-key scales of FP8 keys).
+template <class C>
+struct TileBuf {
+    char k[2][C::TILE_BYTES];
+    float scale[2][TILE_KEYS];
+};
+
 // Each of the FUSED_THREADS threads moves EPT consecutive elements of one key
-// (thread -> key tid/8, part tid%8), widening FP8 to the MFMA operand type.
+// (thread -> key tid/8, part tid%8), widening FP8 to the MFMA operand type;
+// threads 0..63 also move the tile's per-key scales.
 template <class C>
 struct KStage {
     static constexpr int RB = C::EPT * C::kbytes;  // raw bytes per thread
     static constexpr int NV = RB >= 16 ? RB / 16 : 1;
     u32x4_t v[NV];
     u32x2_t v2;
+    float sc;
 
     __device__ void load(const FusedArgs &a, int64_t key0)
     {
@@ -327,12 +373,18 @@ struct KStage {
         } else {
             v2 = ok ? *reinterpret_cast<const u32x2_t *>(src) : u32x2_t{0u, 0u};
         }
+        if constexpr (C::SCALE) {
+            if (tid < TILE_KEYS) {
+                const int64_t ks = key0 + tid;
+                sc = ks < a.N ? a.k_scale[ks] : 0.f;
+            }
+        }
     }
 
-    __device__ void store(char *ktile) const
+    __device__ void store(TileBuf<C> &tb, int buf) const
     {
         const int tid = threadIdx.x;
-        char *dst = ktile + (tid >> 3) * C::ROWB + (tid & 7) * C::EPT * C::TR::ebytes;
+        char *dst = tb.k[buf] + (tid >> 3) * C::ROWB + (tid & 7) * C::EPT * C::TR::ebytes;
         if constexpr (C::KT == ITK_FP8_E4M3) {
             // EPT fp8 bytes -> EPT 16-bit values
             constexpr int OUTV = C::EPT * 2 / 16;
@@ -348,17 +400,10 @@ struct KStage {
             }
 #pragma unroll
             for (int o = 0; o < OUTV; ++o) {
-                u32x4_t out;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t word = words[o * 2 + (e >> 1)];
-                    const uint32_t b0 = (word >> (16 * (e & 1))) & 0xFFu, b1 = (word >> (16 * (e & 1) + 8)) & 0xFFu;
-                    const uint32_t h0 = C::MT == M_BF16 ? fp8_to_bf16_bits(b0) : fp8_to_f16_bits(b0);
-                    const uint32_t h1 = C::MT == M_BF16 ? fp8_to_bf16_bits(b1) : fp8_to_f16_bits(b1);
-                    out[e] = h0 | (h1 << 16);
-                }
-                reinterpret_cast<u32x4_t *>(dst)[o] = out;
+                const u32x2_t lo = fp8x4_widen<C::MT>(words[o * 2]), hi = fp8x4_widen<C::MT>(words[o * 2 + 1]);
+                reinterpret_cast<u32x4_t *>(dst)[o] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
             }
+            if (tid < TILE_KEYS) tb.scale[buf][tid] = sc;
         } else {
             if constexpr (RB >= 16) {
 #pragma unroll
@@ -369,6 +414,76 @@ struct KStage {
         }
     }
 };
+
+// The pipelined tile scan shared by the sample and main passes.
+//
+// Visits `ntiles` key tiles starting at key `first`, `step` keys apart.  The
+// workgroup stages each tile once into LDS (double-buffered, the next tile's
+// global loads in flight during the current tile's compute); each wave whose
+// query still has valid keys in the tile scores it against its own query.
+// The tile is split into two 32-key blocks with separate accumulators, and
+// every block's MFMAs are issued interleaved with the VALU head reduction of
+// the block before it, so matrix and vector work of one wave overlap.  A
+// tile's scores are therefore complete one block later; visit(key0, s) is
+// called once per scored tile (wave-uniform) with lane l holding the score of
+// key key0 + l (scaled by the per-key FP8 scale), which the visitor must mask
+// against the query's length.  Every thread of the workgroup must call this.
+template <class C, class Visit>
+__device__ __forceinline__ void scan_tiles(const FusedArgs &a, TileBuf<C> &tb, const QFrags<C> &qf, int64_t first,
+                                           int64_t step, int ntiles, bool active, uint32_t L, Visit &&visit)
+{
+    const int lane = (int)lane_id();
+    const_cast<QFrags<C> &>(qf).settle();
+    KStage<C> ks;
+    if (ntiles > 0) {
+        ks.load(a, first);
+        ks.store(tb, 0);
+    }
+    __syncthreads();
+    f32x16_t accA[C::HB], accB[C::HB];
+#pragma unroll
+    for (int hb = 0; hb < C::HB; ++hb) {
+        accA[hb] = f32x16_t{};
+        accB[hb] = f32x16_t{};
+    }
+    float p0 = 0.f, psc = 1.f;
+    int64_t pend = -1;  // key0 of the tile whose block 1 sits in accB
+    for (int it = 0; it < ntiles; ++it) {
+        const int64_t key0 = first + (int64_t)it * step;
+        const int buf = it & 1;
+        if (it + 1 < ntiles) ks.load(a, key0 + step);
+        if (active && key0 < (int64_t)L) {
+            const char *tile = tb.k[buf];
+            typename C::frag b[C::KS];
+            // block 0 of this tile, overlapped with the reduction of block 1
+            // of the previous one
+            load_bfrags<C>(b, tile, 0);
+            mfma_block<C>(accA, qf, b);
+            float p1 = reduce_block<C>(accB, qf.w);
+            sched_block<C>();
+            asm volatile("" : "+v"(p1));  // keep the reduction in this region
+            if (pend >= 0) visit(pend, combine_halves(p0, p1) * psc);
+            // block 1, overlapped with the reduction of block 0
+            load_bfrags<C>(b, tile, 1);
+            mfma_block<C>(accB, qf, b);
+            p0 = reduce_block<C>(accA, qf.w);
+            sched_block<C>();
+            asm volatile("" : "+v"(p0));
+            if constexpr (C::SCALE) psc = tb.scale[buf][lane];
+            pend = key0;
+        } else if (pend >= 0) {
+            const float p1 = reduce_block<C>(accB, qf.w);
+            visit(pend, combine_halves(p0, p1) * psc);
+            pend = -1;
+        }
+        if (it + 1 < ntiles) ks.store(tb, buf ^ 1);
+        __syncthreads();
+    }
+    if (pend >= 0) {
+        const float p1 = reduce_block<C>(accB, qf.w);
+        visit(pend, combine_halves(p0, p1) * psc);
+    }
+}
 
 // Wave-level search: the largest bin b with sum_{b' >= b} hist[b'] >= q,
 // or -1 when the histogram holds fewer than q items.  Lane l owns bins
@@ -412,6 +527,7 @@ struct SampleIter {
     int64_t first_key;  // key of the first sampled tile in the split, or -1
     int64_t stride_keys;
     int64_t end;        // exclusive key bound for the split
+    int ntiles;
 };
 __device__ __forceinline__ SampleIter sample_iter(const FusedArgs &a, int g, int p, uint32_t maxL)
 {
@@ -425,15 +541,16 @@ __device__ __forceinline__ SampleIter sample_iter(const FusedArgs &a, int g, int
     const int64_t t0 = lo / TILE_KEYS;  // first tile of the split (lo is tile aligned)
     int64_t first = t0 + ((phase - t0 % st) % st + st) % st;
     it.first_key = first * TILE_KEYS < hi ? first * TILE_KEYS : -1;
+    it.ntiles = it.first_key >= 0 ? (int)((hi - it.first_key + it.stride_keys - 1) / it.stride_keys) : 0;
+    if (a.force == 1) it.ntiles = 0;
     return it;
 }
 
 template <class C>
 struct FusedSmem {
-    char ktile[2][C::TILE_BYTES];
+    TileBuf<C> tb;
     uint32_t whist[FUSED_WAVES][NBINS];
     Cand stage[FUSED_WAVES][128];
-    uint32_t maxL;
 };
 
 __device__ __forceinline__ uint32_t group_max_len(const FusedArgs &a, int g)
@@ -453,7 +570,7 @@ __device__ __forceinline__ uint32_t group_max_len(const FusedArgs &a, int g)
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
 {
-    __shared__ char ktile[C::TILE_BYTES];
+    __shared__ TileBuf<C> tb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int g, p;
     map_group_split(blockIdx.x, a.G, a.Ps, g, p);
@@ -469,24 +586,12 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
     QFrags<C> qf;
     if (active) qf.load(a, t);
     float mn = __builtin_inff(), mx = -__builtin_inff();
-    if (it.first_key >= 0 && a.force != 1) {
-        for (int64_t key0 = it.first_key; key0 < it.end; key0 += it.stride_keys) {
-            KStage<C> ks;
-            ks.load(a, key0);
-            __syncthreads();
-            ks.store(ktile);
-            __syncthreads();
-            if (active && key0 < (int64_t)L) {
-                float s = tile_scores_lds<C>(qf, ktile);
-                const int64_t key = key0 + lane;
-                if (key < (int64_t)L) {
-                    if constexpr (C::SCALE) s *= a.k_scale[key];
-                    mn = fminf(mn, s);
-                    mx = fmaxf(mx, s);
-                }
-            }
+    scan_tiles<C>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, active, L, [&](int64_t key0, float s) {
+        if (key0 + lane < (int64_t)L) {
+            mn = fminf(mn, s);
+            mx = fmaxf(mx, s);
         }
-    }
+    });
     if (active) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -520,7 +625,7 @@ __device__ __forceinline__ uint32_t bin_of(float b)
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
 {
-    __shared__ char ktile[C::TILE_BYTES];
+    __shared__ TileBuf<C> tb;
     __shared__ uint32_t whist[FUSED_WAVES][NBINS];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int g, p;
@@ -538,25 +643,13 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
     const SampleIter it = sample_iter(a, g, p, maxL);
     QFrags<C> qf;
     if (active) qf.load(a, t);
-    if (it.first_key >= 0 && a.force != 1) {
-        for (int64_t key0 = it.first_key; key0 < it.end; key0 += it.stride_keys) {
-            KStage<C> ks;
-            ks.load(a, key0);
-            __syncthreads();
-            ks.store(ktile);
-            __syncthreads();
-            if (active && key0 < (int64_t)L && bp.z == 0.f) {
-                float s = tile_scores_lds<C>(qf, ktile);
-                const int64_t key = key0 + lane;
-                if (key < (int64_t)L) {
-                    if constexpr (C::SCALE) s *= a.k_scale[key];
-                    atomicAdd(&whist[wave][bin_of(fmaf(s, bp.y, bp.x))], 1u);
-                }
-            }
-        }
-    }
+    // a degenerate sampled range leaves the gate open: nothing to count
+    const bool count = active && bp.z == 0.f;
+    scan_tiles<C>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, count, L, [&](int64_t key0, float s) {
+        if (key0 + lane < (int64_t)L) atomicAdd(&whist[wave][bin_of(fmaf(s, bp.y, bp.x))], 1u);
+    });
     __syncthreads();
-    if (active && bp.z == 0.f) {
+    if (count) {
         for (int i = lane; i < NBINS; i += 64) {
             const uint32_t c = whist[wave][i];
             if (c) atomicAdd(&a.hist[(size_t)t * NBINS + i], c);
@@ -565,7 +658,6 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
 }
 
 // ------------------------------------------------ main pass: filter scan
-constexpr int REFRESH_TILES = 8;
 
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
@@ -605,66 +697,69 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
     }
     QFrags<C> qf;
     if (active) qf.load(a, t);
-    uint32_t stage_n = 0, admitted = 0;
+    // Threshold refresh state (wave-uniform): `inrange` counts the admitted
+    // keys whose bin is >= gate_bin, `at_gate` those whose bin == gate_bin.
+    // Whenever the keys strictly above the gate bin number at least k, every
+    // key of the row's Top-k lies above it too, so the gate moves up a bin
+    // (LiteTopK Sec. 3.2: the threshold is the bin holding the k-th largest
+    // score seen so far).
+    uint32_t stage_n = 0, inrange = 0, at_gate = 0;
+    uint32_t tail_reg = 0;  // candidate count when this wave owns the whole row
+    const bool own_row = a.P == 1;
     Cand *cand = a.cand + (size_t)(active ? t : 0) * a.cap;
     const uint32_t cap = (uint32_t)a.cap;
+    const uint32_t kq = (uint32_t)a.k;
+    const bool refresh = delta > 0.f;
 
     auto flush = [&](uint32_t n) {
         uint32_t slot = 0;
-        if (lane == 0) slot = atomicAdd(&a.tail[t], n);
-        slot = __shfl(slot, 0);
+        if (own_row) {
+            slot = tail_reg;
+            tail_reg += n;
+        } else {
+            if (lane == 0) slot = atomicAdd(&a.tail[t], n);
+            slot = __shfl(slot, 0);
+        }
         if ((uint32_t)lane < n && slot + lane < cap) cand[slot + lane] = stage[lane];
     };
 
-    KStage<C> ks;
-    if (ntiles > 0) {
-        ks.load(a, k_lo);
-        ks.store(sm.ktile[0]);
-    }
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        const int64_t key0 = k_lo + (int64_t)it * TILE_KEYS;
-        if (it + 1 < ntiles) ks.load(a, key0 + TILE_KEYS);
-        if (active && key0 < (int64_t)L) {
-            float s = tile_scores_lds<C>(qf, sm.ktile[it & 1]);
-            const int64_t key = key0 + lane;
-            const bool valid = key < (int64_t)L;
-            if constexpr (C::SCALE) s *= valid ? a.k_scale[valid ? key : 0] : 0.f;
-            const float b = fmaf(s, delta, off);
-            const bool pass = valid && b >= gate_f;
-            const uint64_t m = __ballot(pass);
-            if (m) {
-                const uint32_t pos = stage_n + lanes_below(m);
-                if (pass) {
-                    atomicAdd(&whist[bin_of(b)], 1u);
-                    stage[pos] = Cand{(uint32_t)key, s};
-                }
-                const uint32_t n = (uint32_t)__popcll(m);
-                stage_n += n;
-                admitted += n;
-                if (stage_n >= 64u) {
-                    flush(64u);
-                    const bool mv = (uint32_t)lane < stage_n - 64u;
-                    Cand e;
-                    if (mv) e = stage[64 + lane];
-                    if (mv) stage[lane] = e;
-                    stage_n -= 64u;
-                }
+    scan_tiles<C>(a, sm.tb, qf, k_lo, TILE_KEYS, ntiles, active, L, [&](int64_t key0, float s) {
+        const int64_t key = key0 + lane;
+        const bool valid = key < (int64_t)L;
+        const float b = fmaf(s, delta, off);
+        const bool pass = valid && b >= gate_f;
+        const uint64_t m = __ballot(pass);
+        if (m) {
+            const uint32_t bin = bin_of(b);
+            const uint32_t pos = stage_n + lanes_below(m);
+            if (pass) {
+                atomicAdd(&whist[bin], 1u);
+                stage[pos] = Cand{(uint32_t)key, s};
             }
-            if ((it % REFRESH_TILES) == REFRESH_TILES - 1 && admitted >= (uint32_t)a.k && delta > 0.f) {
-                // Threshold refresh: the bin holding the k-th largest score
-                // seen so far is a lower bound of the row's k-th largest bin.
-                const int T = wave_top_bin(whist, (uint32_t)a.k);
-                if (T > gate_bin) {
-                    gate_bin = T;
-                    gate_f = (float)gate_bin;
-                }
+            const uint32_t n = (uint32_t)__popcll(m);
+            stage_n += n;
+            inrange += n;
+            at_gate += (uint32_t)__popcll(__ballot(pass && bin == (uint32_t)gate_bin));
+            if (stage_n >= 64u) {
+                flush(64u);
+                const bool mv = (uint32_t)lane < stage_n - 64u;
+                Cand e;
+                if (mv) e = stage[64 + lane];
+                if (mv) stage[lane] = e;
+                stage_n -= 64u;
+            }
+            if (refresh && inrange - at_gate >= kq && gate_bin < NBINS - 1) {
+                do {
+                    inrange -= at_gate;
+                    ++gate_bin;
+                    at_gate = whist[gate_bin];
+                } while (inrange - at_gate >= kq && gate_bin < NBINS - 1);
+                gate_f = (float)gate_bin;
             }
         }
-        if (it + 1 < ntiles) ks.store(sm.ktile[(it + 1) & 1]);
-        __syncthreads();
-    }
+    });
     if (active && stage_n) flush(stage_n);
+    if (active && own_row && lane == 0) a.tail[t] = tail_reg;
 }
 
 // ------------------------------------------- select (+ recovery) per row
