@@ -97,6 +97,18 @@ __device__ __forceinline__ u32x2_t fp8x4_widen(uint32_t word)
 }
 
 // Kernel configuration: Q dtype, K dtype, head blocks, head dim, ReLU.
+//
+// LDS key layout: one staged key row holds ROWB = D * (MFMA operand bytes)
+// bytes in CH 16-byte chunks followed by one 16-byte pad slot (row stride
+// ROWP = ROWB + 16).  The odd number of 16-byte slots per row rotates the
+// LDS banks from row to row, so the 16-byte B-fragment reads of consecutive
+// key rows fall on distinct banks while every read address stays a per-lane
+// base plus a compile-time offset.
+//
+// Staging: 16- and 32-bit keys are copied global -> LDS by the direct
+// LDS-load path (no registers, no LDS write instructions), in stages of
+// STAGE_KEYS keys; FP8 keys go through registers to be widened once per
+// workgroup, in stages of 64 keys.
 template <int QT_, int KT_, int HB_, int D_, bool RELU_>
 struct FCfg {
     static constexpr int QT = QT_, KT = KT_, HB = HB_, D = D_;
@@ -105,12 +117,19 @@ struct FCfg {
     using TR = MTraits<MT>;
     using frag = typename TR::frag;
     static constexpr int KS = D / TR::kstep;                 // MFMA k-steps
-    static constexpr int ROWB = D * TR::ebytes + TR::pad;    // LDS bytes per staged key
-    static constexpr int TILE_BYTES = TILE_KEYS * ROWB;
+    static constexpr int ROWB = D * TR::ebytes;              // data bytes per staged key
+    static constexpr int CH = ROWB / 16;                     // 16-byte chunks per key row
+    static constexpr int SPR = CH + 1;                       // 16-byte slots per row (with pad)
+    static constexpr int ROWP = SPR * 16;                    // LDS row stride
     static constexpr int kbytes = (KT == ITK_F32) ? 4 : (KT == ITK_FP8_E4M3 ? 1 : 2);
     static constexpr int qbytes = (QT == ITK_F32) ? 4 : 2;
     static constexpr bool SCALE = (KT == ITK_FP8_E4M3);
-    static constexpr int EPT = TILE_KEYS * D / FUSED_THREADS; // staged elements per thread
+    static constexpr bool DMA = !SCALE;
+    static constexpr int STAGE_KEYS = DMA ? (ROWB <= 256 ? 128 : 64) : TILE_KEYS;
+    static constexpr int NSUB = STAGE_KEYS / TILE_KEYS;      // 64-key tiles per stage
+    static constexpr int TILE_LDS = TILE_KEYS * ROWP;        // LDS bytes of one 64-key tile
+    static constexpr int STAGE_BYTES = STAGE_KEYS * ROWP;
+    static constexpr int EPT = TILE_KEYS * D / FUSED_THREADS; // FP8 staging: elements per thread
 };
 
 struct FusedArgs {
@@ -258,49 +277,63 @@ __device__ __forceinline__ float combine_halves(float p0, float p1)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// B fragments of one 32-key block (kb) of a staged tile: lane l supplies key
-// column kb * 32 + l % 32 at the k-slice selected by l / 32.
+// MFMAs of one 32-key block of a staged 64-key tile into acc.  `bl` is the
+// lane's byte address of its first B fragment in the block: lane l supplies
+// key column l % 32 at the k-slice selected by l / 32 (bf16/fp16: 8 values
+// at element 8 (l / 32) of each 16-element step; fp32: element l / 32 of each
+// 2-element step).  The B fragments are read from LDS in chunks of KCH
+// k-steps, at compile-time offsets from `bl`.
 template <class C>
-__device__ __forceinline__ void load_bfrags(typename C::frag (&b)[C::KS], const char *ktile, int kb)
+__device__ __forceinline__ void block_mfma(f32x16_t (&acc)[C::HB], const QFrags<C> &qf, const char *bl)
 {
-    const int l = (int)lane_id();
-    const char *row = ktile + (kb * 32 + (l & 31)) * C::ROWB;
-#pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk) {
-        if constexpr (C::MT == M_F32)
-            b[kk] = *reinterpret_cast<const float *>(row + (kk * 2 + (l >> 5)) * 4);
-        else
-            b[kk] = *reinterpret_cast<const u32x4_t *>(row + (kk * 16 + 8 * (l >> 5)) * 2);
-    }
-}
-
-template <class C>
-__device__ __forceinline__ void mfma_block(f32x16_t (&acc)[C::HB], const QFrags<C> &qf,
-                                           const typename C::frag (&b)[C::KS])
-{
+    constexpr int KCH = C::KS < 8 ? C::KS : 8;
 #pragma unroll
     for (int hb = 0; hb < C::HB; ++hb) acc[hb] = f32x16_t{};
 #pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk)
+    for (int k0 = 0; k0 < C::KS; k0 += KCH) {
+        typename C::frag b[KCH];
 #pragma unroll
-        for (int hb = 0; hb < C::HB; ++hb) acc[hb] = mfma32<C::MT>(qf.q[hb][kk], b[kk], acc[hb]);
+        for (int i = 0; i < KCH; ++i) {
+            const int kk = k0 + i;
+            if constexpr (C::MT == M_F32)
+                b[i] = *reinterpret_cast<const float *>(bl + kk * 8);
+            else
+                b[i] = *reinterpret_cast<const u32x4_t *>(bl + kk * 32);
+        }
+#pragma unroll
+        for (int i = 0; i < KCH; ++i)
+#pragma unroll
+            for (int hb = 0; hb < C::HB; ++hb) acc[hb] = mfma32<C::MT>(qf.q[hb][k0 + i], b[i], acc[hb]);
+    }
 }
 
-// Scheduling hint for one block: the B-fragment LDS reads first, then every
-// MFMA followed by a few VALU instructions of the previous block's head
+// Byte offset of lane l's first B fragment within a staged 64-key tile.
+template <class C>
+__device__ __forceinline__ int bfrag_lane_off()
+{
+    const int l = (int)lane_id();
+    return (l & 31) * C::ROWP + (C::MT == M_F32 ? (l >> 5) * 4 : (l >> 5) * 16);
+}
+
+// Scheduling hint for one block: per chunk, the B-fragment LDS reads, then
+// every MFMA followed by a few VALU instructions of the previous block's head
 // reduction, so that the reduction issues while the matrix core works.
 template <class C>
 __device__ __forceinline__ void sched_block()
 {
+    constexpr int KCH = C::KS < 8 ? C::KS : 8;
     constexpr int NM = C::KS * C::HB;
     constexpr int NV = 32 * C::HB;  // max + fma per accumulator register
     constexpr int PER = (NV + NM - 1) / NM;
 #pragma unroll
-    for (int i = 0; i < C::KS; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int k0 = 0; k0 < C::KS; k0 += KCH) {
 #pragma unroll
-    for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+        for (int i = 0; i < KCH; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int i = 0; i < KCH * C::HB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
+        }
     }
 }
 
@@ -341,22 +374,95 @@ __device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int
 }
 
 // ---------------------------------------------------- tile staging (LDS)
-// Double-buffered key tiles (and the per-key scales of FP8 keys).
+// Double-buffered key stages (and the per-key scales of FP8 keys).
 template <class C>
 struct TileBuf {
-    char k[2][C::TILE_BYTES];
+    char k[2][C::STAGE_BYTES];
     float scale[2][TILE_KEYS];
 };
 
-// Each of the FUSED_THREADS threads moves EPT consecutive elements of one key
-// (thread -> key tid/8, part tid%8), widening FP8 to the MFMA operand type;
-// threads 0..63 also move the tile's per-key scales.
+// One wave instruction of the direct global -> LDS copy: lane i's 16 bytes
+// at `src` land at LDS byte lds_base + 16 i (lds_base is wave-uniform and
+// goes through M0, which is restored afterwards).  Issued from inline
+// assembly so that the compiler does not fence later LDS accesses of other
+// buffers on it; the caller waits for completion (vmcnt) before the barrier
+// that publishes the stage.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds_base)
+        : "memory");
+}
+
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(T *p)
+{
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) char *)p;
+}
+
+// Direct global -> LDS copy of a stage of NSUB * 64 keys.  The stage's LDS
+// image is NSUB * 64 * SPR 16-byte slots, copied in 1 KB pieces (one wave
+// instruction each: lane i writes slot 64 j + i of piece j); piece j goes to
+// wave j % 8.  Slot q holds chunk q % SPR of row q / SPR; the pad slot of a
+// row re-reads the row's first chunk.  The per-lane source offsets within
+// the stage are fixed, so they are computed once (DmaPlan); keys past N
+// re-read key N-1 (their scores are never used).
+template <class C, int NSUB>
+struct DmaPlan {
+    static constexpr int PIECES = NSUB * TILE_KEYS * C::SPR / 64;
+    static constexpr int PER_WAVE = (PIECES + FUSED_WAVES - 1) / FUSED_WAVES;
+    static_assert(PIECES * 64 == NSUB * TILE_KEYS * C::SPR, "stage must split into 1 KB pieces");
+    int src_off[PER_WAVE];  // row * ROWB + chunk * 16
+    int row[PER_WAVE];
+
+    __device__ void init()
+    {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int q = (j * FUSED_WAVES + wave) * 64 + lane;
+            const int r = q / C::SPR, c = q % C::SPR;
+            row[j] = r;
+            src_off[j] = r * C::ROWB + (c < C::CH ? c : 0) * 16;
+        }
+    }
+
+    __device__ __forceinline__ void issue(const FusedArgs &a, TileBuf<C> &tb, int buf, int64_t key0) const
+    {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const uint32_t base = lds_addr(tb.k[buf]);
+        const char *kbase = static_cast<const char *>(a.K) + (size_t)key0 * C::ROWB;
+        const bool tail = key0 + NSUB * TILE_KEYS > a.N;
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int piece = j * FUSED_WAVES + wave;
+            if (piece < PIECES) {
+                const char *src = kbase + src_off[j];
+                if (tail && key0 + row[j] >= a.N)
+                    src = static_cast<const char *>(a.K) + (size_t)(a.N - 1) * C::ROWB + (src_off[j] - row[j] * C::ROWB);
+                lds_dma16(src, base + (uint32_t)piece * 1024u);
+            }
+        }
+    }
+};
+
+// FP8 staging through registers: each of the FUSED_THREADS threads moves
+// EPT consecutive elements of one key of a 64-key tile (thread -> key tid/8,
+// part tid%8), widening them to the MFMA operand type; threads 0..63 also
+// move the tile's per-key scales.
 template <class C>
 struct KStage {
     static constexpr int RB = C::EPT * C::kbytes;  // raw bytes per thread
-    static constexpr int NV = RB >= 16 ? RB / 16 : 1;
-    u32x4_t v[NV];
-    u32x2_t v2;
+    static_assert(!C::SCALE || RB == 8 || RB == 16 || RB == 32, "unsupported FP8 staging width");
+    static constexpr int NW = C::SCALE ? RB / 4 : 2;
+    uint32_t words[NW];
     float sc;
 
     __device__ void load(const FusedArgs &a, int64_t key0)
@@ -366,79 +472,71 @@ struct KStage {
         const int part = tid & 7;
         const bool ok = key < a.N;
         const char *src = static_cast<const char *>(a.K) + ((size_t)(ok ? key : 0) * C::D + part * C::EPT) * C::kbytes;
-        if constexpr (RB >= 16) {
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
-                v[i] = ok ? reinterpret_cast<const u32x4_t *>(src)[i] : u32x4_t{0u, 0u, 0u, 0u};
-        } else {
-            v2 = ok ? *reinterpret_cast<const u32x2_t *>(src) : u32x2_t{0u, 0u};
+        for (int i = 0; i < NW; i += 2) {
+            const u32x2_t v = ok ? reinterpret_cast<const u32x2_t *>(src)[i / 2] : u32x2_t{0u, 0u};
+            words[i] = v[0];
+            words[i + 1] = v[1];
         }
-        if constexpr (C::SCALE) {
-            if (tid < TILE_KEYS) {
-                const int64_t ks = key0 + tid;
-                sc = ks < a.N ? a.k_scale[ks] : 0.f;
-            }
+        if (tid < TILE_KEYS) {
+            const int64_t ks = key0 + tid;
+            sc = ks < a.N ? a.k_scale[ks] : 0.f;
         }
     }
 
     __device__ void store(TileBuf<C> &tb, int buf) const
     {
         const int tid = threadIdx.x;
-        char *dst = tb.k[buf] + (tid >> 3) * C::ROWB + (tid & 7) * C::EPT * C::TR::ebytes;
-        if constexpr (C::KT == ITK_FP8_E4M3) {
-            // EPT fp8 bytes -> EPT 16-bit values
-            constexpr int OUTV = C::EPT * 2 / 16;
-            uint32_t words[C::EPT / 4];
-            if constexpr (RB >= 16) {
+        const int r = tid >> 3, part = tid & 7;
+        // EPT fp8 values -> EPT 16-bit values = EPT / 8 chunks of 16 bytes
 #pragma unroll
-                for (int i = 0; i < NV; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) words[i * 4 + j] = v[i][j];
-            } else {
-                words[0] = v2[0];
-                words[1] = v2[1];
-            }
-#pragma unroll
-            for (int o = 0; o < OUTV; ++o) {
-                const u32x2_t lo = fp8x4_widen<C::MT>(words[o * 2]), hi = fp8x4_widen<C::MT>(words[o * 2 + 1]);
-                reinterpret_cast<u32x4_t *>(dst)[o] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-            }
-            if (tid < TILE_KEYS) tb.scale[buf][tid] = sc;
-        } else {
-            if constexpr (RB >= 16) {
-#pragma unroll
-                for (int i = 0; i < NV; ++i) reinterpret_cast<u32x4_t *>(dst)[i] = v[i];
-            } else {
-                *reinterpret_cast<u32x2_t *>(dst) = v2;
-            }
+        for (int o = 0; o < C::EPT / 8; ++o) {
+            const u32x2_t lo = fp8x4_widen<C::MT>(words[o * 2]), hi = fp8x4_widen<C::MT>(words[o * 2 + 1]);
+            const int c = part * (C::EPT / 8) + o;
+            *reinterpret_cast<u32x4_t *>(tb.k[buf] + r * C::ROWP + c * 16) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
+        if (tid < TILE_KEYS) tb.scale[buf][tid] = sc;
     }
 };
 
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
 // The pipelined tile scan shared by the sample and main passes.
 //
-// Visits `ntiles` key tiles starting at key `first`, `step` keys apart.  The
-// workgroup stages each tile once into LDS (double-buffered, the next tile's
-// global loads in flight during the current tile's compute); each wave whose
-// query still has valid keys in the tile scores it against its own query.
-// The tile is split into two 32-key blocks with separate accumulators, and
-// every block's MFMAs are issued interleaved with the VALU head reduction of
-// the block before it, so matrix and vector work of one wave overlap.  A
-// tile's scores are therefore complete one block later; visit(key0, s) is
-// called once per scored tile (wave-uniform) with lane l holding the score of
-// key key0 + l (scaled by the per-key FP8 scale), which the visitor must mask
-// against the query's length.  Every thread of the workgroup must call this.
-template <class C, class Visit>
+// Visits `nstages` stages of NSUB consecutive 64-key tiles, the first at key
+// `first` and each `step` keys after the previous one; tiles at or beyond
+// `key_end` are skipped.  The workgroup stages each stage once into LDS
+// (double-buffered: the next stage's copy is in flight during the current
+// stage's compute); each wave whose query still has valid keys in a tile
+// scores it against its own query.  A tile is split into two 32-key blocks
+// with separate accumulators, and every block's MFMAs are issued interleaved
+// with the VALU head reduction of the block before it, so matrix and vector
+// work of one wave overlap.  A tile's scores are therefore complete one block
+// later; visit(key0, s) is called once per scored tile (wave-uniform) with
+// lane l holding the score of key key0 + l (scaled by the per-key FP8 scale),
+// which the visitor must mask against the query's length.  Every thread of
+// the workgroup must call this.
+template <class C, int NSUB, class Visit>
 __device__ __forceinline__ void scan_tiles(const FusedArgs &a, TileBuf<C> &tb, const QFrags<C> &qf, int64_t first,
-                                           int64_t step, int ntiles, bool active, uint32_t L, Visit &&visit)
+                                           int64_t step, int nstages, int64_t key_end, bool active, uint32_t L,
+                                           Visit &&visit)
 {
+    static_assert(C::DMA || NSUB == 1, "FP8 staging moves one 64-key tile per stage");
     const int lane = (int)lane_id();
-    const_cast<QFrags<C> &>(qf).settle();
+    const int64_t kend = key_end < (int64_t)L ? key_end : (int64_t)L;
     KStage<C> ks;
-    if (ntiles > 0) {
-        ks.load(a, first);
-        ks.store(tb, 0);
+    DmaPlan<C, NSUB> dp;
+    if constexpr (C::DMA) dp.init();
+    if (nstages > 0) {
+        if constexpr (C::DMA) {
+            dp.issue(a, tb, 0, first);
+        } else {
+            ks.load(a, first);
+            ks.store(tb, 0);
+        }
     }
+    const_cast<QFrags<C> &>(qf).settle();
+    wait_vmem_all();
     __syncthreads();
     f32x16_t accA[C::HB], accB[C::HB];
 #pragma unroll
@@ -448,35 +546,43 @@ __device__ __forceinline__ void scan_tiles(const FusedArgs &a, TileBuf<C> &tb, c
     }
     float p0 = 0.f, psc = 1.f;
     int64_t pend = -1;  // key0 of the tile whose block 1 sits in accB
-    for (int it = 0; it < ntiles; ++it) {
-        const int64_t key0 = first + (int64_t)it * step;
-        const int buf = it & 1;
-        if (it + 1 < ntiles) ks.load(a, key0 + step);
-        if (active && key0 < (int64_t)L) {
-            const char *tile = tb.k[buf];
-            typename C::frag b[C::KS];
-            // block 0 of this tile, overlapped with the reduction of block 1
-            // of the previous one
-            load_bfrags<C>(b, tile, 0);
-            mfma_block<C>(accA, qf, b);
-            float p1 = reduce_block<C>(accB, qf.w);
-            sched_block<C>();
-            asm volatile("" : "+v"(p1));  // keep the reduction in this region
-            if (pend >= 0) visit(pend, combine_halves(p0, p1) * psc);
-            // block 1, overlapped with the reduction of block 0
-            load_bfrags<C>(b, tile, 1);
-            mfma_block<C>(accB, qf, b);
-            p0 = reduce_block<C>(accA, qf.w);
-            sched_block<C>();
-            asm volatile("" : "+v"(p0));
-            if constexpr (C::SCALE) psc = tb.scale[buf][lane];
-            pend = key0;
-        } else if (pend >= 0) {
-            const float p1 = reduce_block<C>(accB, qf.w);
-            visit(pend, combine_halves(p0, p1) * psc);
-            pend = -1;
+    const int boff = bfrag_lane_off<C>();
+    for (int st = 0; st < nstages; ++st) {
+        const int64_t skey = first + (int64_t)st * step;
+        const int buf = st & 1;
+        if (st + 1 < nstages) {
+            if constexpr (C::DMA) dp.issue(a, tb, buf ^ 1, skey + step);
+            else ks.load(a, skey + step);
         }
-        if (it + 1 < ntiles) ks.store(tb, buf ^ 1);
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) {
+            const int64_t key0 = skey + sub * TILE_KEYS;
+            if (active && key0 < kend) {
+                const char *bl = tb.k[buf] + boff + sub * C::TILE_LDS;
+                // block 0 of this tile, overlapped with the reduction of
+                // block 1 of the previous one
+                block_mfma<C>(accA, qf, bl);
+                float p1 = reduce_block<C>(accB, qf.w);
+                sched_block<C>();
+                asm volatile("" : "+v"(p1));  // keep the reduction in this region
+                if (pend >= 0) visit(pend, combine_halves(p0, p1) * psc);
+                // block 1, overlapped with the reduction of block 0
+                block_mfma<C>(accB, qf, bl + 32 * C::ROWP);
+                p0 = reduce_block<C>(accA, qf.w);
+                sched_block<C>();
+                asm volatile("" : "+v"(p0));
+                if constexpr (C::SCALE) psc = tb.scale[buf][lane];
+                pend = key0;
+            } else if (pend >= 0) {
+                const float p1 = reduce_block<C>(accB, qf.w);
+                visit(pend, combine_halves(p0, p1) * psc);
+                pend = -1;
+            }
+        }
+        if (st + 1 < nstages) {
+            if constexpr (!C::DMA) ks.store(tb, buf ^ 1);
+            wait_vmem_all();
+        }
         __syncthreads();
     }
     if (pend >= 0) {
@@ -546,13 +652,6 @@ __device__ __forceinline__ SampleIter sample_iter(const FusedArgs &a, int g, int
     return it;
 }
 
-template <class C>
-struct FusedSmem {
-    TileBuf<C> tb;
-    uint32_t whist[FUSED_WAVES][NBINS];
-    Cand stage[FUSED_WAVES][128];
-};
-
 __device__ __forceinline__ uint32_t group_max_len(const FusedArgs &a, int g)
 {
     uint32_t m = 0;
@@ -586,7 +685,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
     QFrags<C> qf;
     if (active) qf.load(a, t);
     float mn = __builtin_inff(), mx = -__builtin_inff();
-    scan_tiles<C>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, active, L, [&](int64_t key0, float s) {
+    scan_tiles<C, 1>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, it.end, active, L, [&](int64_t key0, float s) {
         if (key0 + lane < (int64_t)L) {
             mn = fminf(mn, s);
             mx = fmaxf(mx, s);
@@ -645,7 +744,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
     if (active) qf.load(a, t);
     // a degenerate sampled range leaves the gate open: nothing to count
     const bool count = active && bp.z == 0.f;
-    scan_tiles<C>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, count, L, [&](int64_t key0, float s) {
+    scan_tiles<C, 1>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, it.end, count, L, [&](int64_t key0, float s) {
         if (key0 + lane < (int64_t)L) atomicAdd(&whist[wave][bin_of(fmaf(s, bp.y, bp.x))], 1u);
     });
     __syncthreads();
@@ -662,7 +761,11 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
 {
-    __shared__ FusedSmem<C> sm;
+    // Separate LDS objects, so that the compiler can tell the histogram and
+    // staging accesses apart from the in-flight key-tile copies.
+    __shared__ TileBuf<C> tb;
+    __shared__ uint32_t whist_all[FUSED_WAVES][NBINS];
+    __shared__ Cand stage_all[FUSED_WAVES][128];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int g, p;
     map_group_split(blockIdx.x, a.G, a.P, g, p);
@@ -674,10 +777,10 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
     const int64_t k_lo = (int64_t)p * a.span;
     int64_t k_hi = k_lo + a.span;
     if (k_hi > (int64_t)maxL) k_hi = maxL;
-    const int ntiles = k_hi > k_lo ? (int)((k_hi - k_lo + TILE_KEYS - 1) / TILE_KEYS) : 0;
+    const int nstages = k_hi > k_lo ? (int)((k_hi - k_lo + C::STAGE_KEYS - 1) / C::STAGE_KEYS) : 0;
 
-    uint32_t *whist = sm.whist[wave];
-    Cand *stage = sm.stage[wave];
+    uint32_t *whist = whist_all[wave];
+    Cand *stage = stage_all[wave];
     for (int i = lane; i < NBINS; i += 64) whist[i] = 0u;
 
     // Initial threshold bin from the sample (wave-uniform state).
@@ -723,7 +826,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
         if ((uint32_t)lane < n && slot + lane < cap) cand[slot + lane] = stage[lane];
     };
 
-    scan_tiles<C>(a, sm.tb, qf, k_lo, TILE_KEYS, ntiles, active, L, [&](int64_t key0, float s) {
+    scan_tiles<C, C::NSUB>(a, tb, qf, k_lo, C::STAGE_KEYS, nstages, k_hi, active, L, [&](int64_t key0, float s) {
         const int64_t key = key0 + lane;
         const bool valid = key < (int64_t)L;
         const float b = fmaf(s, delta, off);
