@@ -30,13 +30,17 @@ __global__ void k_debug_fp8(const uint8_t *in, uint16_t *bf, uint16_t *hf, int n
     }
 }
 
-__global__ void k_debug_coarse(const float *x, uint32_t *key, float *endpoint, int n)
+__global__ void k_debug_coarse(const float *x, uint32_t *key, int n)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) {
-        key[i] = coarse_key(x[i]);
-        endpoint[i] = coarse_endpoint((uint32_t)i);
-    }
+    if (i < n) key[i] = coarse_key(x[i]);
+}
+
+// One wave per bin: the endpoint exactly as the standalone scan computes it.
+__global__ void k_debug_endpoint(float *endpoint)
+{
+    const float e = coarse_endpoint_wave(blockIdx.x);
+    if (threadIdx.x == 0) endpoint[blockIdx.x] = e;
 }
 
 }  // namespace itk
@@ -75,7 +79,9 @@ itk_status itk_debug_coarse(const float *x, uint32_t *key_out, float *endpoint_o
 {
     if (!x || !key_out || !endpoint_out || n <= 0 || n > NBINS) return ITK_ERR_INVALID_ARG;
     hipLaunchKernelGGL(k_debug_coarse, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), x,
-                       key_out, endpoint_out, n);
+                       key_out, n);
+    if (hipGetLastError() != hipSuccess) return ITK_ERR_HIP;
+    hipLaunchKernelGGL(k_debug_endpoint, dim3(n), dim3(64), 0, static_cast<hipStream_t>(stream), endpoint_out);
     return hipGetLastError() == hipSuccess ? ITK_OK : ITK_ERR_HIP;
 }
 

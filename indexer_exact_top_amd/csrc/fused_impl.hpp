@@ -606,12 +606,7 @@ __device__ int wave_top_bin(HistPtr hist, uint32_t q)
         c[i] = hist[hi - 1 - i];
         s += c[i];
     }
-    uint32_t incl = s;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (l >= off) incl += o;
-    }
+    const uint32_t incl = wave_incl_sum(s);
     const uint64_t m = __ballot(incl >= q);
     if (!m) return -1;
     const int f = __ffsll((unsigned long long)m) - 1;
@@ -625,7 +620,7 @@ __device__ int wave_top_bin(HistPtr hist, uint32_t q)
             cum += c[i];
         }
     }
-    return __shfl(bin, f);
+    return (int)lane_value((uint32_t)bin, f);
 }
 
 // Keys of sampled tile number `m` (0-based within the split's sampled tiles).
@@ -692,11 +687,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
         }
     });
     if (active) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            mn = fminf(mn, __shfl_xor(mn, off));
-            mx = fmaxf(mx, __shfl_xor(mx, off));
-        }
+        mn = wave_min(mn);
+        mx = wave_max(mx);
         if (lane == 0) a.mm[(size_t)t * a.Ps + p] = make_float2(mn, mx);
     }
 }
@@ -821,7 +813,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
             tail_reg += n;
         } else {
             if (lane == 0) slot = atomicAdd(&a.tail[t], n);
-            slot = __shfl(slot, 0);
+            slot = lane_value(slot, 0);
         }
         if ((uint32_t)lane < n && slot + lane < cap) cand[slot + lane] = stage[lane];
     };
@@ -934,7 +926,28 @@ __global__ __launch_bounds__(SEL_THREADS) void k_fused_select(FusedArgs a)
     };
     if (!recover) {
         CandSrc src{a.cand + (size_t)t * a.cap, n};
-        exact_select<SEL_THREADS>(sm, src, need, emit);
+        if (n <= (uint32_t)STASH_CAP) {
+            // all candidates fit on chip: one parallel copy, then every
+            // refinement round reads LDS only
+            constexpr int B = 8;  // loads in flight per thread
+            for (uint32_t i0 = 0; i0 < n; i0 += SEL_THREADS * B) {
+                Cand e[B];
+#pragma unroll
+                for (int j = 0; j < B; ++j) {
+                    const uint32_t i = i0 + j * SEL_THREADS + tid;
+                    if (i < n) e[j] = src.c[i];
+                }
+#pragma unroll
+                for (int j = 0; j < B; ++j) {
+                    const uint32_t i = i0 + j * SEL_THREADS + tid;
+                    if (i < n) sm.stash[i] = make_key(e[j].val, e[j].idx);
+                }
+            }
+            __syncthreads();
+            select_stashed<SEL_THREADS>(sm, n, need, emit);
+        } else {
+            exact_select<SEL_THREADS>(sm, src, need, emit);
+        }
     } else {
         RescoreSrc<C> src{&a, t, L};
         exact_select<SEL_THREADS>(sm, src, need, emit);

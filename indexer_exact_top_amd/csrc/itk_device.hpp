@@ -21,7 +21,8 @@ namespace itk {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int NBINS = 2048;       // one 2^11-bin histogram, reused by every round
-constexpr int STASH_CAP = 4096;   // boundary-group entries kept on chip
+constexpr int STASH_CAP = 7680;   // items kept on chip (60 KB of composite keys)
+constexpr int BOUND_CAP = 1024;   // boundary-bin items kept for the final exact rounds
 
 // ----------------------------------------------------------------- keys
 // Order-preserving map fp32 -> u32 (larger value -> larger key).  -0 is
@@ -74,20 +75,36 @@ __device__ __forceinline__ uint32_t coarse_key(float x)
     return o >> 5;
 }
 
+__device__ __forceinline__ uint32_t lane_id_early() { return __lane_id(); }
+
 // Smallest fp32 value x (over [-inf, +inf]) with coarse_key(x) >= tau: then
 // "x >= endpoint" reproduces "coarse_key(x) >= tau" with one compare.  Bins
 // above the bin of +inf hold only NaN codes; their endpoint is NaN, which
-// admits no value.
-__device__ inline float coarse_endpoint(uint32_t tau)
+// admits no value.  Searched by one whole wave: every round splits the open
+// interval (lo, hi] of ordered keys into 64 parts, each lane tests one split
+// point, and the lowest passing part becomes the new interval (coarse_key is
+// monotone, so the predicate is a step function of the ordered key).  Six
+// rounds resolve 32 bits.  All lanes of the wave must call it; every lane
+// gets the result.
+__device__ inline float coarse_endpoint_wave(uint32_t tau)
 {
     uint32_t lo = ordered_key(-__builtin_inff());
     uint32_t hi = ordered_key(__builtin_inff());
     if (coarse_key(from_ordered_key(lo)) >= tau) return -__builtin_inff();
     if (coarse_key(from_ordered_key(hi)) < tau) return __builtin_nanf("");
+    const uint32_t l = lane_id_early();
     while (hi - lo > 1u) {  // coarse(lo) < tau <= coarse(hi)
-        const uint32_t mid = lo + ((hi - lo) >> 1);
-        if (coarse_key(from_ordered_key(mid)) >= tau) hi = mid;
-        else lo = mid;
+        const uint64_t span = (uint64_t)(hi - lo);
+        // split points lo + span*(l+1)/64 for l = 0..62 (lane 63 is hi itself)
+        const uint32_t pt = l < 63u ? lo + (uint32_t)((span * (l + 1u)) >> 6) : hi;
+        const bool ok = pt > lo && coarse_key(from_ordered_key(pt)) >= tau;
+        const uint64_t m = __ballot(ok);            // lane 63 always passes
+        const int f = __ffsll((unsigned long long)m) - 1;
+        const uint32_t new_hi = (uint32_t)__builtin_amdgcn_readlane((int)pt, f);
+        uint32_t new_lo = (uint32_t)__builtin_amdgcn_readlane((int)pt, f > 0 ? f - 1 : 0);
+        if (f == 0 || new_lo <= lo) new_lo = lo;
+        lo = new_lo;
+        hi = new_hi;
     }
     return from_ordered_key(hi);
 }
@@ -100,6 +117,70 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Cross-lane steps in registers (DPP), not through LDS: row_shr:n moves each
+// lane's value n lanes up within its row of 16, row_bcast:15 / row_bcast:31
+// hand lane 15 / 31 to the following rows.  Lanes without a source take
+// `identity`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t identity)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: lane l gets sum_{l' <= l} v.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v)
+{
+    v += dpp_u32<0x111, 0xF>(v, 0u);  // row_shr:1
+    v += dpp_u32<0x112, 0xF>(v, 0u);  // row_shr:2
+    v += dpp_u32<0x114, 0xF>(v, 0u);  // row_shr:4
+    v += dpp_u32<0x118, 0xF>(v, 0u);  // row_shr:8
+    v += dpp_u32<0x142, 0xA>(v, 0u);  // row_bcast:15 into rows 1, 3
+    v += dpp_u32<0x143, 0xC>(v, 0u);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Inclusive suffix sum over the lanes of a wave: lane l gets sum_{l' >= l} v.
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v)
+{
+    const uint32_t incl = wave_incl_sum(v);
+    return lane_value(incl, 63) - incl + v;
+}
+
+// Wave-wide min / max of a float (every lane gets the result).
+__device__ __forceinline__ float wave_min(float x)
+{
+    const uint32_t inf = __float_as_uint(__builtin_inff());
+    uint32_t v = __float_as_uint(x);
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(dpp_u32<0x111, 0xF>(v, inf))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(dpp_u32<0x112, 0xF>(v, inf))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(dpp_u32<0x114, 0xF>(v, inf))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(dpp_u32<0x118, 0xF>(v, inf))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(dpp_u32<0x142, 0xA>(v, inf))));
+    v = __float_as_uint(fminf(__uint_as_float(v), __uint_as_float(dpp_u32<0x143, 0xC>(v, inf))));
+    return __uint_as_float(lane_value(v, 63));
+}
+__device__ __forceinline__ float wave_max(float x) { return -wave_min(-x); }
+
+// Reserve `count` consecutive slots per lane from an LDS or global counter
+// with one atomic per wave; returns the lane's first slot.  Every lane of the
+// wave must call it (count may be 0).
+__device__ __forceinline__ uint32_t wave_reserve_n(uint32_t count, uint32_t *ctr)
+{
+    const uint32_t incl = wave_incl_sum(count);
+    const uint32_t total = lane_value(incl, 63);
+    uint32_t base = 0;
+    if (total) {
+        if (lane_id() == 0u) base = atomicAdd(ctr, total);
+        base = lane_value(base, 0);
+    }
+    return base + incl - count;
+}
+
 // Reserve one slot per active lane with `pred` from an LDS or global counter,
 // with one atomic per wave.  Must be reached by every active lane.
 __device__ __forceinline__ uint32_t wave_reserve(bool pred, uint32_t *ctr)
@@ -109,21 +190,9 @@ __device__ __forceinline__ uint32_t wave_reserve(bool pred, uint32_t *ctr)
     if (m) {
         const int leader = __ffsll((unsigned long long)m) - 1;
         if ((int)lane_id() == leader) base = atomicAdd(ctr, (uint32_t)__popcll(m));
-        base = __shfl(base, leader);
+        base = lane_value(base, leader);
     }
     return base + lanes_below(m);
-}
-
-// Inclusive suffix sum over the lanes of a wave: lane l gets sum_{l' >= l} v.
-__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v)
-{
-    const int l = (int)lane_id();
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(v, off);
-        if (l + off < 64) v += o;
-    }
-    return v;
 }
 
 // ------------------------------------------------- block boundary search
@@ -187,6 +256,9 @@ __device__ void find_boundary(const uint32_t *hist, uint32_t quota, uint32_t *sc
 struct SelectSmem {
     uint32_t hist[NBINS];
     uint64_t stash[STASH_CAP];
+    uint64_t bound[BOUND_CAP];
+    float vmin[16], vmax[16];
+    uint32_t n_bound;
     uint64_t P, M;        // resolved prefix and its mask
     uint32_t quota;       // items still to take from the current region
     uint32_t level;
@@ -201,18 +273,22 @@ struct SelectSmem {
 // over the threads of the block (every thread must call for_each; it may
 // contain barriers).  `emit(slot, K)` receives each selected key once, with
 // slots 0..need-1 in unspecified order.  Requires 1 <= need <= #items.
+// When `prestashed` >= 0 the caller has already put all `prestashed` items'
+// keys into sm.stash (and synchronized), and `src` is never read.
 //
 // Rounds: histogram the next digit of the items in the current region, find
 // the boundary digit, commit strictly better digits, retain the boundary
 // group.  As soon as the boundary group fits STASH_CAP it is copied on chip
 // (and everything above it emitted) so that later rounds never touch `src`.
 template <int NT, class Src, class Emit>
-__device__ void exact_select(SelectSmem &sm, Src &src, uint32_t need, Emit &&emit)
+__device__ void exact_select(SelectSmem &sm, Src &src, uint32_t need, Emit &&emit, int prestashed = -1)
 {
     const int tid = threadIdx.x;
     if (tid == 0) {
         sm.P = 0; sm.M = 0; sm.quota = need; sm.level = 0;
-        sm.done = 0; sm.stashed = 0; sm.stash_n = 0; sm.out_n = 0;
+        sm.done = 0; sm.out_n = 0;
+        sm.stashed = prestashed >= 0 ? 1u : 0u;
+        sm.stash_n = prestashed >= 0 ? (uint32_t)prestashed : 0u;
     }
     __syncthreads();
     for (;;) {
@@ -282,6 +358,136 @@ __device__ void exact_select(SelectSmem &sm, Src &src, uint32_t need, Emit &&emi
             __syncthreads();
         }
     }
+}
+
+// Item source of exact_select calls that start from a filled stash.
+struct NoSrc {
+    template <class F>
+    __device__ void for_each(F &&) const {}
+};
+
+// Exact Top-`need` of the `n` items whose composite keys the caller has put
+// into sm.stash (n <= STASH_CAP, 1 <= need <= n, followed by a barrier).
+//
+// A value histogram first narrows the problem: NBINS equal-width bins over
+// the items' own [min, max] (a monotone map of the value, so the order of
+// bins is the order of values), the boundary bin b where the count from the
+// top reaches `need`, every item of a better bin emitted at once, and the
+// items of bin b gathered.  Only those go through the composite-key radix
+// rounds (value digits, then inverted-index digits), which settle the exact
+// boundary including the lower-index rule for equal values.  When the range
+// is degenerate or the boundary bin is too large to gather, the radix rounds
+// run over all n items instead.
+template <int NT, class Emit>
+__device__ void select_stashed(SelectSmem &sm, uint32_t n, uint32_t need, Emit &&emit)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    NoSrc nosrc;
+    // value range
+    // every loop below reads its LDS items in batches of SB per thread, so
+    // that a thread waits for one LDS round trip per batch, not per item
+    constexpr int SB = 4;
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    for (uint32_t i0 = tid; i0 < n; i0 += SB * NT) {
+        float v[SB];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const uint32_t i = i0 + j * NT;
+            v[j] = i < n ? key_value(sm.stash[i]) : __builtin_nanf("");
+        }
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            mn = fminf(mn, v[j]);  // fminf/fmaxf ignore the NaN padding
+            mx = fmaxf(mx, v[j]);
+        }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+        sm.vmin[wave] = mn;
+        sm.vmax[wave] = mx;
+    }
+    for (int i = tid; i < NBINS; i += NT) sm.hist[i] = 0u;
+    if (tid == 0) sm.n_bound = 0;
+    __syncthreads();
+    mn = sm.vmin[0];
+    mx = sm.vmax[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) {
+        mn = fminf(mn, sm.vmin[w]);
+        mx = fmaxf(mx, sm.vmax[w]);
+    }
+    const float scale = (float)NBINS / (mx - mn);
+    const bool binned = mx > mn && __builtin_isfinite(scale) && scale > 0.f && __builtin_isfinite(mn);
+    if (!binned) {
+        exact_select<NT>(sm, nosrc, need, emit, (int)n);
+        return;
+    }
+    auto bin_of_value = [&](float v) {
+        return (uint32_t)fminf(fmaxf(floorf((v - mn) * scale), 0.f), (float)(NBINS - 1));
+    };
+    for (uint32_t i0 = tid; i0 < n; i0 += SB * NT) {
+        uint32_t b[SB];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const uint32_t i = i0 + j * NT;
+            b[j] = i < n ? bin_of_value(key_value(sm.stash[i])) : NBINS;
+        }
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+            if (b[j] < (uint32_t)NBINS) atomicAdd(&sm.hist[b[j]], 1u);
+    }
+    __syncthreads();
+    find_boundary<NT>(sm.hist, need, sm.scan, &sm.b);
+    const uint32_t B = sm.b.digit, above = sm.b.above, eq = sm.b.eq;
+    if (eq > (uint32_t)BOUND_CAP) {
+        exact_select<NT>(sm, nosrc, need, emit, (int)n);
+        return;
+    }
+    if (tid == 0) sm.out_n = 0;
+    __syncthreads();
+    {
+        // count this thread's items above / at the boundary bin, reserve the
+        // slots once, then write them
+        uint32_t nt = 0, nk = 0;
+        for (uint32_t i0 = tid; i0 < n; i0 += SB * NT) {
+            uint32_t b[SB];
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const uint32_t i = i0 + j * NT;
+                b[j] = i < n ? bin_of_value(key_value(sm.stash[i])) : 0u;
+                nt += i < n && b[j] > B;
+                nk += i < n && b[j] == B;
+            }
+        }
+        uint32_t st = wave_reserve_n(nt, &sm.out_n);
+        uint32_t sk = wave_reserve_n(nk, &sm.n_bound);
+        for (uint32_t i0 = tid; i0 < n; i0 += SB * NT) {
+            uint64_t K[SB];
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const uint32_t i = i0 + j * NT;
+                K[j] = i < n ? sm.stash[i] : 0ull;
+            }
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                if (i0 + j * NT >= n) continue;
+                const uint32_t b = bin_of_value(key_value(K[j]));
+                if (b > B) emit(st++, K[j]);
+                else if (b == B) sm.bound[sk++] = K[j];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t q = need - above;  // 1 <= q <= eq
+    if (q == eq) {
+        for (uint32_t i = tid; i < eq; i += NT) emit(above + i, sm.bound[i]);
+        __syncthreads();
+        return;
+    }
+    for (uint32_t i = tid; i < eq; i += NT) sm.stash[i] = sm.bound[i];
+    __syncthreads();
+    exact_select<NT>(sm, nosrc, q, [&](uint32_t slot, uint64_t K) { emit(above + slot, K); }, (int)eq);
 }
 
 }  // namespace itk

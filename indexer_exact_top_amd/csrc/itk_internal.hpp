@@ -36,6 +36,8 @@ RouteSink &route_sink();
 // --------------------------------------------------------------- ragged
 constexpr int RAG_THREADS = 256;
 constexpr int RAG_WAVES = RAG_THREADS / 64;
+constexpr int RAG_MAX_CELLS = 64;
+constexpr int FIN_THREADS = 1024;  // ragged finisher: one workgroup per row  // (segment, wave) cells per row whose candidates the finisher gathers on chip
 
 struct RaggedPlan {
     int32_t M = 0;
@@ -59,7 +61,7 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
 constexpr int FUSED_WAVES = 8;                  // queries per workgroup
 constexpr int FUSED_THREADS = FUSED_WAVES * 64;
 constexpr int TILE_KEYS = 64;
-constexpr int SEL_THREADS = 256;
+constexpr int SEL_THREADS = 512;   // fused select: one workgroup per row
 
 struct FusedPlan {
     int32_t T = 0, H = 0, D = 0, k = 0;

@@ -81,9 +81,17 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
     const uint32_t phase = (uint32_t)r % sb;
     const uint32_t nb_total = (L + 15u) >> 4;
     const uint32_t nvb = nb_total > phase ? (nb_total - 1u - phase) / sb + 1u : 0u;
-    for (uint32_t e = tid; e < nvb * 16u; e += RAG_THREADS) {
-        const uint32_t i = (phase + (e >> 4) * sb) * 16u + (e & 15u);
-        if (i < L) atomicAdd(&hist[coarse_key(row[i])], 1u);
+    for (uint32_t e0 = 0; e0 < nvb * 16u; e0 += RAG_THREADS * 8u) {
+        float x[8];  // all of a thread's view loads in flight at once
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t e = e0 + j * RAG_THREADS + tid;
+            const uint32_t i = (phase + (e >> 4) * sb) * 16u + (e & 15u);
+            x[j] = (e < nvb * 16u && i < L) ? row[i] : __builtin_nanf("");
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (x[j] == x[j]) atomicAdd(&hist[coarse_key(x[j])], 1u);
     }
     __syncthreads();
     uint32_t n_a = 0;
@@ -99,12 +107,12 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
         find_boundary<RAG_THREADS>(hist, q0, scan_tmp, &b0);
         find_boundary<RAG_THREADS>(hist, q1, scan_tmp, &b1);
     }
-    if (tid == 0) {
-        s_e[0] = admit_all ? -__builtin_inff() : coarse_endpoint(b0.digit);
-        s_e[1] = admit_all ? -__builtin_inff() : coarse_endpoint(b1.digit);
-        if (p == 0) a.ep[r] = make_float4(s_e[0], s_e[1], admit_all ? 1.f : 0.f, 0.f);
+    if (wave < 2) {  // wave 0: primary endpoint, wave 1: secondary
+        const float e = admit_all ? -__builtin_inff() : coarse_endpoint_wave(wave == 0 ? b0.digit : b1.digit);
+        if (lane == 0) s_e[wave] = e;
     }
     __syncthreads();
+    if (tid == 0 && p == 0) a.ep[r] = make_float4(s_e[0], s_e[1], admit_all ? 1.f : 0.f, 0.f);
     const float e0 = s_e[0], e1 = s_e[1];
 
     // ---- Phase 2: certify + collect over [seg_lo, seg_hi).
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
     };
     if (seg_hi > seg_lo) {
         if (VEC) {
-            constexpr int U = 4;
+            constexpr int U = 16;  // all of a thread's 16-byte loads in flight at once
             const uint32_t n4 = (uint32_t)((seg_hi - seg_lo) >> 2);
             const f32x4_t *v4 = reinterpret_cast<const f32x4_t *>(row + seg_lo);
             for (uint32_t base = 0; base < n4; base += RAG_THREADS * U) {
@@ -216,34 +224,96 @@ struct RowSrc {
 
 enum { ROUTE_SAMPLE = 1, ROUTE_BAND = 2, ROUTE_EXACT = 3, ROUTE_ALL = 4 };
 
-__global__ __launch_bounds__(RAG_THREADS) void k_ragged_finish(RaggedArgs a, int vec)
+// Copies every candidate of a row (slices in cell order, then the band
+// slice) into the on-chip stash as composite keys; returns the count.  The
+// caller guarantees that the count fits STASH_CAP.  Cell offsets come from a
+// wave prefix sum over the per-cell counts; then each wave copies whole
+// cells, with all of a lane's loads issued before any is consumed, so the
+// copy costs about one memory round trip instead of one per item.
+__device__ uint32_t gather_candidates(const SliceSrc &src, SelectSmem &sm, uint32_t *cpre)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < 64) {
+        uint32_t carry = 0;
+        for (int base = 0; base < src.ncells; base += 64) {
+            const int c = base + lane;
+            const uint32_t v = c < src.ncells ? min(src.cnt[c], src.subcap) : 0u;
+            const uint32_t incl = wave_incl_sum(v);
+            if (c < src.ncells) cpre[c + 1] = carry + incl;
+            carry += lane_value(incl, 63);
+        }
+        if (tid == 0) cpre[0] = 0;
+    }
+    __syncthreads();
+    const uint32_t nslice = cpre[src.ncells], total = nslice + src.band_n;
+    constexpr int B = 8;  // loads in flight per lane
+    for (int c = wave; c < src.ncells; c += blockDim.x >> 6) {
+        const uint32_t lo = cpre[c], n = cpre[c + 1] - lo;
+        const Cand *cell = src.slices + (size_t)c * src.subcap;
+        for (uint32_t i0 = 0; i0 < n; i0 += 64 * B) {
+            Cand e[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const uint32_t i = i0 + j * 64 + lane;
+                if (i < n) e[j] = cell[i];
+            }
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const uint32_t i = i0 + j * 64 + lane;
+                if (i < n) sm.stash[lo + i] = make_key(e[j].val, e[j].idx);
+            }
+        }
+    }
+    for (uint32_t i0 = 0; i0 < src.band_n; i0 += blockDim.x * B) {
+        Cand e[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const uint32_t i = i0 + j * blockDim.x + tid;
+            if (i < src.band_n) e[j] = src.band[i];
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const uint32_t i = i0 + j * blockDim.x + tid;
+            if (i < src.band_n) sm.stash[nslice + i] = make_key(e[j].val, e[j].idx);
+        }
+    }
+    __syncthreads();
+    return total;
+}
+
+__global__ __launch_bounds__(FIN_THREADS) void k_ragged_finish(RaggedArgs a, int vec)
 {
     __shared__ SelectSmem sm;
     __shared__ uint32_t s_c0, s_c1, s_ovf, s_band_n;
     __shared__ int s_route;
+    __shared__ uint32_t cpre[RAG_MAX_CELLS + 1];
 
     const int tid = threadIdx.x;
     const int r = blockIdx.x;
+    const int ncells = a.P * RAG_WAVES;
+    const size_t cell0 = (size_t)r * ncells;
+    // independent loads first: one memory round trip for all of them
     const uint32_t L = row_length(a, r);
+    const float4 ep = a.ep[r];
+    const bool has_cell = tid < ncells;
+    const uint32_t my_cnt = has_cell ? a.cnt[cell0 + tid] : 0u;
+    const uint32_t my_c1 = has_cell ? a.c1[cell0 + tid] : 0u;
     const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
     int32_t *out = a.out_idx + (size_t)r * a.k;
-    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += RAG_THREADS) out[i] = -1;
+    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += FIN_THREADS) out[i] = -1;
     if (need == 0) {
         if (tid == 0 && a.route) a.route[r] = ROUTE_ALL;
         return;
     }
     if (tid == 0) { s_c0 = 0; s_c1 = 0; s_ovf = 0; s_band_n = 0; }
     __syncthreads();
-    const int ncells = a.P * RAG_WAVES;
-    const size_t cell0 = (size_t)r * ncells;
-    for (int c = tid; c < ncells; c += RAG_THREADS) {
-        const uint32_t n = a.cnt[cell0 + c];
+    for (int c = tid; c < ncells; c += FIN_THREADS) {
+        const uint32_t n = c == tid ? my_cnt : a.cnt[cell0 + c];
         atomicAdd(&s_c0, n);
-        atomicAdd(&s_c1, a.c1[cell0 + c]);
+        atomicAdd(&s_c1, c == tid ? my_c1 : a.c1[cell0 + c]);
         if (n > (uint32_t)a.subcap) atomicOr(&s_ovf, 1u);
     }
     __syncthreads();
-    const float4 ep = a.ep[r];
     const float *row = a.scores + (size_t)r * (size_t)a.pitch;
     if (tid == 0) {
         const uint32_t C0 = s_c0, C1 = s_c1;
@@ -275,11 +345,18 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_finish(RaggedArgs a, int
     };
     if (route == ROUTE_EXACT) {
         RowSrc src{row, L, vec != 0};
-        exact_select<RAG_THREADS>(sm, src, need, emit);
+        exact_select<FIN_THREADS>(sm, src, need, emit);
     } else {
         SliceSrc src{a.slices + cell0 * (size_t)a.subcap, a.cnt + cell0, ncells, (uint32_t)a.subcap,
-                     a.band + (size_t)r * a.bandcap, route == ROUTE_BAND ? s_band_n : 0u};
-        exact_select<RAG_THREADS>(sm, src, need, emit);
+                     a.band + (size_t)r * a.bandcap, route == ROUTE_BAND ? min(s_band_n, (uint32_t)a.bandcap) : 0u};
+        // the slices hold at most C0 (route 1) or C1 (route 2) entries
+        const uint32_t bound = route == ROUTE_BAND ? s_c1 : s_c0;
+        if (bound <= (uint32_t)STASH_CAP && ncells <= RAG_MAX_CELLS) {
+            const uint32_t n = gather_candidates(src, sm, cpre);
+            select_stashed<FIN_THREADS>(sm, n, need, emit);
+        } else {
+            exact_select<FIN_THREADS>(sm, src, need, emit);
+        }
     }
     if (tid == 0 && a.route) a.route[r] = route;
 }
@@ -354,7 +431,7 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
     if (e != hipSuccess) return e;
     {
         StageTimer st(ST_RAG_FINISH, stream);
-        hipLaunchKernelGGL(k_ragged_finish, dim3(p.M), dim3(RAG_THREADS), 0, stream, a, vec ? 1 : 0);
+        hipLaunchKernelGGL(k_ragged_finish, dim3(p.M), dim3(FIN_THREADS), 0, stream, a, vec ? 1 : 0);
     }
     return hipGetLastError();
 }
