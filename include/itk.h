@@ -105,6 +105,10 @@ itk_status topk_ragged(const float *scores, int64_t row_pitch, const int32_t *ro
  *   H > 32 needs D <= 128; F32 needs ceil(H/32) * D <= 128.
  *   Scores are accumulated in fp32 (MFMA); selection is exact on those fp32
  *   scores.  Scratch is O(T * k): see the workspace size query.
+ *   With H == 1 and 16-bit inputs the scores come from a separate kernel
+ *   family (queries as MFMA columns, 512 per workgroup); its workspace also
+ *   holds every query's sampled-view scores (at most about 32768 per query).
+ *   Results follow the same contract on either path.
  *   workspace: as for topk_ragged.
  * ------------------------------------------------------------------------ */
 size_t indexer_topk_fused_workspace_size(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k,

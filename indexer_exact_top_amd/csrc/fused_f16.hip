@@ -1,11 +1,17 @@
 // Fused Indexer-TopK instantiations with fp16 queries (fp16 or e4m3fn keys).
-#include "fused_impl.hpp"
+#include "fused_qrow.hpp"
 
 namespace itk {
 FusedLauncher find_fused_launcher_f16(int qt, int kt, int hb, int d, bool relu)
 {
     ITK_FUSED_CASES_FOR(ITK_F16, ITK_F16)
     ITK_FUSED_CASES_FOR(ITK_F16, ITK_FP8_E4M3)
+    return nullptr;
+}
+FusedLauncher find_qrow_launcher_f16(int qt, int kt, int d, bool relu)
+{
+    ITK_QROW_CASES_FOR(ITK_F16, ITK_F16)
+    ITK_QROW_CASES_FOR(ITK_F16, ITK_FP8_E4M3)
     return nullptr;
 }
 }  // namespace itk

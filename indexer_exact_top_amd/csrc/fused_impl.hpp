@@ -145,9 +145,13 @@ struct FusedArgs {
     float2 *mm;        // [T][Ps] {min, max} of the sampled scores
     uint32_t *hist;    // [T][NBINS] sample histogram
     uint32_t *tail;    // [T] candidates appended (may exceed cap)
-    Cand *cand;        // [T][cap]
-    int64_t N, span, span_s;
-    int32_t T, H, k, cap, G, P, Ps, sample_tiles, force;
+    Cand *cand;        // [T][cap] (head rows) or [T][P][capS] (single head)
+    // single-head (query-column) path
+    float *samp;       // [T][samp_cap] scores of the sampled view
+    float *gate;       // [T] admission gate (score space)
+    uint32_t *qcnt;    // [T][P] candidates per (query, key split); may exceed capS
+    int64_t N, span, span_s, samp_cap;
+    int32_t T, H, k, cap, capS, G, P, Ps, sample_tiles, force;
     float rho;
 };
 
@@ -375,11 +379,21 @@ __device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int
 
 // ---------------------------------------------------- tile staging (LDS)
 // Double-buffered key stages (and the per-key scales of FP8 keys).
-template <class C>
+template <class C, int NB = 2>
 struct TileBuf {
-    char k[2][C::STAGE_BYTES];
-    float scale[2][TILE_KEYS];
+    static constexpr int nbuf = NB;
+    char k[NB][C::STAGE_BYTES];
+    char sink[1024];            // target of the padding copies (never read)
+    float scale[2][TILE_KEYS];  // FP8 keys (register staging, two buffers)
 };
+
+// s_waitcnt vmcnt(N) (other counters untouched).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // One wave instruction of the direct global -> LDS copy: lane i's 16 bytes
 // at `src` land at LDS byte lds_base + 16 i (lds_base is wave-uniform and
@@ -434,7 +448,12 @@ struct DmaPlan {
         }
     }
 
-    __device__ __forceinline__ void issue(const FusedArgs &a, TileBuf<C> &tb, int buf, int64_t key0) const
+    // With more than two stage buffers every wave issues exactly PER_WAVE copy
+    // instructions per stage (pieces past the stage re-copy the first key row
+    // into tb.sink), so that a wave's count of copies in flight is a
+    // compile-time multiple of PER_WAVE.
+    template <int NB>
+    __device__ __forceinline__ void issue(const FusedArgs &a, TileBuf<C, NB> &tb, int buf, int64_t key0) const
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const uint32_t base = lds_addr(tb.k[buf]);
@@ -448,6 +467,8 @@ struct DmaPlan {
                 if (tail && key0 + row[j] >= a.N)
                     src = static_cast<const char *>(a.K) + (size_t)(a.N - 1) * C::ROWB + (src_off[j] - row[j] * C::ROWB);
                 lds_dma16(src, base + (uint32_t)piece * 1024u);
+            } else if constexpr (NB > 2) {
+                lds_dma16(static_cast<const char *>(a.K) + (threadIdx.x & 63) * 16 % C::ROWB, lds_addr(tb.sink));
             }
         }
     }

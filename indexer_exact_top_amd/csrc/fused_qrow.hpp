@@ -1,0 +1,608 @@
+// Fused score + exact Top-k for single-head scoring (H == 1), e.g. inner-
+// product retrieval (LiteTopK, arXiv 2607.11976, Sec. 3.1 Eq. (2)) or a
+// one-head indexer (Sec. 2.1 Eq. (1) with H_I = 1).
+//
+// With one head per query, the head-rows mapping of fused_impl.hpp would fill
+// one of the 32 MFMA rows.  Here the roles are turned around: the MFMA A
+// operand is a block of 32 keys (rows, staged in LDS exactly as in the
+// head-rows kernels), the B operand a block of 32 queries (columns, held in
+// VGPRs), so every MFMA computes 32 x 32 useful scores.  A wave owns QROW_QB
+// such query blocks, so each staged key fragment feeds QROW_QB MFMAs.  In the
+// accumulator layout lane l holds query column l % 32 and 16 key rows, so a
+// lane's per-query state (weight, length, gate) is one register per block.
+//
+// Steps (same method as the head-rows path, re-mapped):
+//  * sample: the tile-strided view of every query is scored and stored
+//    (bounded per query); one workgroup per query then places the gate at the
+//    bin of the view's rank-q score, q = ceil(rho * k * n_view / L), with
+//    m = 2048 equal-width bins over the view's range (the rank calibration of
+//    the Sample-Guided paper, arXiv 2609.08450, Sec. 4.2);
+//  * scan: every key of the query's range is scored, and a key is admitted
+//    when its score is >= the query's gate; admitted keys go to a per-
+//    (query, key split) slice, with slots from a per-wave LDS counter;
+//  * select: one workgroup per query gathers its slices on chip and selects
+//    exactly; a query whose slices overflowed or hold fewer than min(k, L)
+//    candidates is re-scored and selected from its full row.
+#pragma once
+
+#include "fused_impl.hpp"
+
+namespace itk {
+
+constexpr int QROW_QB = 2;                      // 32-query blocks per wave
+constexpr int QROW_QPW = 32 * QROW_QB;          // queries per wave
+constexpr int QROW_Q = QROW_QPW * FUSED_WAVES;  // queries per workgroup
+
+// Per-lane query state: lane l owns query column l % 32 of every block.
+template <class C>
+struct QRowQ {
+    typename C::frag q[QROW_QB][C::KS];  // B fragments (8 values at k-slice l / 32)
+    float w[QROW_QB];
+    uint32_t L[QROW_QB];
+    int t[QROW_QB];
+
+    __device__ void load(const FusedArgs &a, int g)
+    {
+        const int l = (int)lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int qb = 0; qb < QROW_QB; ++qb) {
+            t[qb] = g * QROW_Q + wave * QROW_QPW + qb * 32 + (l & 31);
+            const bool act = t[qb] < a.T;
+            w[qb] = act ? a.W[t[qb]] : 0.f;
+            L[qb] = act ? kv_length(a, t[qb]) : 0u;
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk) {
+                const int d0 = kk * 16 + 8 * (l >> 5);
+                const char *ptr = static_cast<const char *>(a.Q) + ((size_t)(act ? t[qb] : 0) * C::D + d0) * 2;
+                q[qb][kk] = act ? *reinterpret_cast<const u32x4_t *>(ptr) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+
+    __device__ __forceinline__ void settle()
+    {
+#pragma unroll
+        for (int qb = 0; qb < QROW_QB; ++qb) {
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk) asm volatile("" : "+v"(q[qb][kk]));
+            asm volatile("" : "+v"(w[qb]));
+        }
+    }
+};
+
+// Score of one accumulator value: w * ReLU(q . k) (or w * q . k without
+// ReLU), times the key's FP8 scale.  The same expression is used by every
+// route, so a key's score does not depend on the route.
+template <class C>
+__device__ __forceinline__ float qrow_score(float acc, float w, float scale)
+{
+    float s = (C::RELU ? relu_bits(acc) : acc) * w;
+    if constexpr (C::SCALE) s *= scale;
+    return s;
+}
+
+// Key row held by accumulator register r of lane l, relative to the block.
+__device__ __forceinline__ int qrow_key_of(int r, int l)
+{
+    return 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+}
+
+// MFMAs of one 32-key block: keys (A, from LDS at the lane's fragment address
+// `al`) against the lane's query blocks (B, registers).
+template <class C>
+__device__ __forceinline__ void qrow_block_mfma(f32x16_t (&acc)[QROW_QB], const QRowQ<C> &qq, const char *al)
+{
+    constexpr int KCH = C::KS < 8 ? C::KS : (C::KS >= 16 ? 4 : 8);  // register budget at D = 256
+#pragma unroll
+    for (int qb = 0; qb < QROW_QB; ++qb) acc[qb] = f32x16_t{};
+#pragma unroll
+    for (int k0 = 0; k0 < C::KS; k0 += KCH) {
+        typename C::frag a[KCH];
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) a[i] = *reinterpret_cast<const u32x4_t *>(al + (k0 + i) * 32);
+#pragma unroll
+        for (int i = 0; i < KCH; ++i)
+#pragma unroll
+            for (int qb = 0; qb < QROW_QB; ++qb) acc[qb] = mfma32<C::MT>(a[i], qq.q[qb][k0 + i], acc[qb]);
+    }
+}
+
+// Per-key FP8 scales of the 16 keys a lane holds in a block (4 groups of 4
+// consecutive keys).
+template <class C>
+__device__ __forceinline__ void qrow_block_scales(float (&sc)[16], const float *tile_scale, int blk)
+{
+    const int l = (int)lane_id();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(tile_scale + blk * 32 + 8 * g + 4 * (l >> 5));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[4 * g + j] = v[j];
+    }
+}
+
+// Stage buffers of the QRow scan (16-/32-bit keys; FP8 keys go through
+// registers with two buffers).  Deeper copy pipelines (4 buffers, 3 stages in
+// flight) measured no faster on 4M x 256 fp16 keys.
+constexpr int QROW_NB = 2;
+template <class C>
+using QRowTiles = TileBuf<C, C::DMA ? QROW_NB : 2>;
+
+// Waits until at most `n_after` stages' copies of this wave are in flight.
+template <int PW, int NB>
+__device__ __forceinline__ void wait_stages_after(int n_after)
+{
+    static_assert(NB <= 4, "wait table");
+    if (n_after <= 0) wait_vmem_le<0>();
+    else if (n_after == 1) wait_vmem_le<PW>();
+    else wait_vmem_le<2 * PW>();
+}
+
+// The pipelined QRow scan: `nstages` stages of NSUB 64-key tiles, the first
+// at key `first`, `step` keys apart, keys at or beyond `key_end` skipped.
+// visit(kb0, acc, sc) is called once per computed 32-key block (wave-uniform)
+// with the block's first key and the accumulators (and FP8 scales).  Every
+// thread of the workgroup must call this.
+template <class C, int NSUB, class Visit>
+__device__ __forceinline__ void qrow_scan(const FusedArgs &a, QRowTiles<C> &tb, const QRowQ<C> &qq, int64_t first,
+                                          int64_t step, int nstages, int64_t key_end, uint32_t wave_maxL,
+                                          Visit &&visit)
+{
+    static_assert(C::DMA || NSUB == 1, "FP8 staging moves one 64-key tile per stage");
+    constexpr int NB = QRowTiles<C>::nbuf;
+    constexpr int PW = DmaPlan<C, NSUB>::PER_WAVE;
+    const int64_t kend = key_end < (int64_t)wave_maxL ? key_end : (int64_t)wave_maxL;
+    KStage<C> ks;
+    DmaPlan<C, NSUB> dp;
+    if constexpr (C::DMA) dp.init();
+    const int pre = nstages < NB - 1 ? nstages : NB - 1;  // stages in flight before the loop
+    if constexpr (C::DMA) {
+        for (int s0 = 0; s0 < pre; ++s0) dp.issue(a, tb, s0, first + (int64_t)s0 * step);
+    } else if (nstages > 0) {
+        ks.load(a, first);
+        ks.store(tb, 0);
+    }
+    const_cast<QRowQ<C> &>(qq).settle();
+    if constexpr (C::DMA) wait_stages_after<PW, NB>(pre - 1);
+    else wait_vmem_all();
+    __syncthreads();
+    const int boff = bfrag_lane_off<C>();
+    for (int st = 0; st < nstages; ++st) {
+        const int64_t skey = first + (int64_t)st * step;
+        const int buf = st % NB;
+        if constexpr (C::DMA) {
+            if (st + NB - 1 < nstages) dp.issue(a, tb, (st + NB - 1) % NB, skey + (int64_t)(NB - 1) * step);
+        } else if (st + 1 < nstages) {
+            ks.load(a, skey + step);
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2 * NSUB; ++blk) {
+            const int64_t kb0 = skey + blk * 32;
+            if (kb0 < kend) {
+                f32x16_t acc[QROW_QB];
+                qrow_block_mfma<C>(acc, qq, tb.k[buf] + boff + blk * 32 * C::ROWP);
+                float sc[16];
+                if constexpr (C::SCALE) qrow_block_scales<C>(sc, tb.scale[buf], blk);
+                visit(kb0, acc, sc);
+            }
+        }
+        if (st + 1 < nstages) {
+            if constexpr (C::DMA) {
+                // stage st+1 complete; stages st+2 .. issued may stay in flight
+                const int last_issued = (st + NB - 1 < nstages ? st + NB - 1 : nstages - 1);
+                wait_stages_after<PW, NB>(last_issued - (st + 1));
+            } else {
+                ks.store(tb, buf ^ 1);
+                wait_vmem_all();
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<0x111, 0xF>(v, 0u));
+    v = max(v, dpp_u32<0x112, 0xF>(v, 0u));
+    v = max(v, dpp_u32<0x114, 0xF>(v, 0u));
+    v = max(v, dpp_u32<0x118, 0xF>(v, 0u));
+    v = max(v, dpp_u32<0x142, 0xA>(v, 0u));
+    v = max(v, dpp_u32<0x143, 0xC>(v, 0u));
+    return lane_value(v, 63);
+}
+
+// ------------------------------------------------ sample: score the view
+template <class C>
+__global__ __launch_bounds__(FUSED_THREADS) void k_qrow_sample(FusedArgs a)
+{
+    __shared__ QRowTiles<C> tb;
+    const int l = (int)lane_id();
+    int g, p;
+    map_group_split(blockIdx.x, a.G, a.Ps, g, p);
+    QRowQ<C> qq;
+    qq.load(a, g);
+    const uint32_t wave_maxL = wave_max_u32(max(qq.L[0], qq.L[QROW_QB - 1]));
+    uint32_t gmaxL = 0;  // the view of the workgroup's longest query
+    {
+        __shared__ uint32_t s_max;
+        if (threadIdx.x == 0) s_max = 0;
+        __syncthreads();
+        if (l == 0) atomicMax(&s_max, wave_maxL);
+        __syncthreads();
+        gmaxL = s_max;
+    }
+    const SampleIter it = sample_iter(a, g, p, gmaxL);
+    const int64_t st = a.sample_tiles;
+    const int64_t phase = g % a.sample_tiles;
+    qrow_scan<C, 1>(a, tb, qq, it.first_key, it.stride_keys, it.ntiles, it.end, gmaxL,
+                    [&](int64_t kb0, const f32x16_t (&acc)[QROW_QB], const float (&sc)[16]) {
+                        // view position of key kb0: sampled tile ordinal * 64 + offset
+                        const int64_t tile = kb0 / TILE_KEYS;
+                        const int64_t vpos0 = ((tile - phase) / st) * TILE_KEYS + (kb0 - tile * TILE_KEYS);
+#pragma unroll
+                        for (int qb = 0; qb < QROW_QB; ++qb) {
+                            if (qq.t[qb] >= a.T) continue;
+                            float *row = a.samp + (size_t)qq.t[qb] * a.samp_cap;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int kr = qrow_key_of(r, l);
+                                if (kb0 + kr < (int64_t)qq.L[qb])
+                                    row[vpos0 + kr] = qrow_score<C>(acc[qb][r], qq.w[qb], sc[r]);
+                            }
+                        }
+                    });
+}
+
+// ------------------------------- gate: one workgroup per query, from the view
+template <class C>
+__global__ __launch_bounds__(SEL_THREADS) void k_qrow_gate(FusedArgs a)
+{
+    constexpr int NT = SEL_THREADS;
+    __shared__ uint32_t hist[NBINS];
+    __shared__ uint32_t scan[16];
+    __shared__ float red[2][16];
+    __shared__ BoundaryOut bo;
+    const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint32_t L = kv_length(a, t);
+    const int g = t / QROW_Q;
+    const RowSample rs = row_sample(a, g, L, false);
+    // per-call reset of the query's slice counters
+    for (int p = tid; p < 2 * a.P; p += NT) a.qcnt[(size_t)t * a.P * 2 + p] = 0u;
+    if (rs.admit_all) {
+        if (tid == 0) a.gate[t] = -__builtin_inff();
+        return;
+    }
+    const float *row = a.samp + (size_t)t * a.samp_cap;
+    const uint32_t n = rs.n_a;
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    for (uint32_t i0 = tid; i0 < n; i0 += 8 * NT) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t i = i0 + j * NT;
+            v[j] = i < n ? row[i] : __builtin_nanf("");
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            mn = fminf(mn, v[j]);
+            mx = fmaxf(mx, v[j]);
+        }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+        red[0][wave] = mn;
+        red[1][wave] = mx;
+    }
+    for (int i = tid; i < NBINS; i += NT) hist[i] = 0u;
+    __syncthreads();
+    mn = red[0][0];
+    mx = red[1][0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) {
+        mn = fminf(mn, red[0][w]);
+        mx = fmaxf(mx, red[1][w]);
+    }
+    const float scale = (float)NBINS / (mx - mn);
+    if (!(mx > mn) || !__builtin_isfinite(scale) || !(scale > 0.f) || !__builtin_isfinite(mn)) {
+        if (tid == 0) a.gate[t] = -__builtin_inff();
+        return;
+    }
+    for (uint32_t i0 = tid; i0 < n; i0 += 8 * NT) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t i = i0 + j * NT;
+            v[j] = i < n ? row[i] : __builtin_nanf("");
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (v[j] == v[j])
+                atomicAdd(&hist[(uint32_t)fminf(fmaxf(floorf((v[j] - mn) * scale), 0.f), (float)(NBINS - 1))], 1u);
+    }
+    __syncthreads();
+    find_boundary<NT>(hist, rs.q0, scan, &bo);
+    if (tid == 0) {
+        // every view score in bins >= the boundary bin is >= this value
+        const float edge = bo.digit ? mn + (float)bo.digit / scale : -__builtin_inff();
+        a.gate[t] = bo.digit ? fminf(edge, mx) : -__builtin_inff();
+    }
+}
+
+// ------------------------------------------------ scan: gate and collect
+template <class C>
+__global__ __launch_bounds__(FUSED_THREADS) void k_qrow_main(FusedArgs a)
+{
+    __shared__ QRowTiles<C> tb;
+    const int tid = threadIdx.x, l = tid & 63;
+    int g, p;
+    map_group_split(blockIdx.x, a.G, a.P, g, p);
+    if (a.force == 1) return;  // every query takes the re-scoring route
+    QRowQ<C> qq;
+    qq.load(a, g);
+    float gate[QROW_QB];
+    int64_t kend[QROW_QB];
+    const int64_t k_lo = (int64_t)p * a.span;
+    int64_t k_hi = k_lo + a.span;
+    uint32_t wmax = 0;
+#pragma unroll
+    for (int qb = 0; qb < QROW_QB; ++qb) {
+        const bool act = qq.t[qb] < a.T;
+        gate[qb] = act ? a.gate[qq.t[qb]] : __builtin_inff();
+        kend[qb] = (int64_t)qq.L[qb] < k_hi ? (int64_t)qq.L[qb] : k_hi;
+        wmax = max(wmax, qq.L[qb]);
+    }
+    __shared__ uint32_t s_max;
+    if (tid == 0) s_max = 0;
+    __syncthreads();
+    wmax = wave_max_u32(wmax);
+    if (l == 0) atomicMax(&s_max, wmax);
+    __syncthreads();
+    const uint32_t gmaxL = s_max;
+    if (k_hi > (int64_t)gmaxL) k_hi = gmaxL;
+    const int nstages = k_hi > k_lo ? (int)((k_hi - k_lo + C::STAGE_KEYS - 1) / C::STAGE_KEYS) : 0;
+    // keys below kmin are valid for every lane's queries (wave-uniform)
+    uint32_t kmin_l = 0xFFFFFFFFu;
+#pragma unroll
+    for (int qb = 0; qb < QROW_QB; ++qb)
+        kmin_l = min(kmin_l, (uint32_t)(kend[qb] > k_lo ? kend[qb] - k_lo : 0));
+    const uint32_t kmin = ~wave_max_u32(~kmin_l);  // wave minimum
+    // Each lane appends to its own half of the (query, split) slice, with a
+    // register counter: lanes l and l + 32 hold different keys of the same
+    // query, so their halves never collide and no atomics are needed.
+    const uint32_t capH = (uint32_t)a.capS / 2u;
+    const int h = l >> 5;
+    Cand *myslice[QROW_QB];
+    uint32_t cnt[QROW_QB];
+#pragma unroll
+    for (int qb = 0; qb < QROW_QB; ++qb) {
+        const int tq = qq.t[qb] < a.T ? qq.t[qb] : 0;
+        myslice[qb] = a.cand + (((size_t)tq * a.P + p) * 2 + h) * capH;
+        cnt[qb] = 0;
+    }
+
+    qrow_scan<C, C::NSUB>(a, tb, qq, k_lo, C::STAGE_KEYS, nstages, k_hi, gmaxL,
+                          [&](int64_t kb0, const f32x16_t (&acc)[QROW_QB], const float (&sc)[16]) {
+                              const bool full = kb0 + 32 <= k_lo + (int64_t)kmin;
+                              // valid key rows of this block per query block: row < lim
+                              int32_t lim[QROW_QB];
+#pragma unroll
+                              for (int qb = 0; qb < QROW_QB; ++qb) {
+                                  const int64_t d = kend[qb] - kb0;
+                                  lim[qb] = d < 0 ? 0 : (d > 32 ? 32 : (int32_t)d);
+                              }
+#pragma unroll
+                              for (int qb = 0; qb < QROW_QB; ++qb) {
+#pragma unroll
+                                  for (int r = 0; r < 16; ++r) {
+                                      const float s = qrow_score<C>(acc[qb][r], qq.w[qb], sc[r]);
+                                      const int kr = qrow_key_of(r, l);
+                                      const bool pass = s >= gate[qb] && (full || kr < lim[qb]);
+                                      if (pass) {
+                                          if (cnt[qb] < capH) myslice[qb][cnt[qb]] = Cand{(uint32_t)kb0 + (uint32_t)kr, s};
+                                          ++cnt[qb];
+                                      }
+                                  }
+                              }
+                          });
+#pragma unroll
+    for (int qb = 0; qb < QROW_QB; ++qb)
+        if (qq.t[qb] < a.T) a.qcnt[((size_t)qq.t[qb] * a.P + p) * 2 + h] = cnt[qb];
+}
+
+// ------------------------------------------- select (+ recovery) per query
+// Every valid key of query t, re-scored with the same operand layout as the
+// scan (the query in column 0 of the B operand, 32 keys per MFMA as rows), so
+// that every score equals the scan's.  Lanes 0 and 32 hold the results.
+template <class C>
+struct QRowRescoreSrc {
+    const FusedArgs *a;
+    int t;
+    uint32_t L;
+    template <class F>
+    __device__ void for_each(F &&f) const
+    {
+        const int l = (int)lane_id();
+        const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+        const float w = a->W[t];
+        typename C::frag qf[C::KS];
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk) {
+            const int d0 = kk * 16 + 8 * (l >> 5);
+            qf[kk] = (l & 31) == 0 ? *reinterpret_cast<const u32x4_t *>(static_cast<const char *>(a->Q) +
+                                                                          ((size_t)t * C::D + d0) * 2)
+                                   : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        for (int64_t kb0 = (int64_t)wave * 32; kb0 < (int64_t)L; kb0 += (int64_t)nw * 32) {
+            const int64_t key = kb0 + (l & 31);
+            const bool ok = key < a->N;
+            const char *krow = static_cast<const char *>(a->K) + (size_t)(ok ? key : 0) * C::D * C::kbytes;
+            f32x16_t acc = f32x16_t{};
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk) {
+                const int d0 = kk * 16 + 8 * (l >> 5);
+                u32x4_t af;
+                if constexpr (C::KT == ITK_FP8_E4M3) {
+                    const u32x2_t raw = ok ? *reinterpret_cast<const u32x2_t *>(krow + d0) : u32x2_t{0u, 0u};
+                    const u32x2_t lo = fp8x4_widen<C::MT>(raw[0]), hi = fp8x4_widen<C::MT>(raw[1]);
+                    af = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+                } else {
+                    af = ok ? *reinterpret_cast<const u32x4_t *>(krow + d0 * 2) : u32x4_t{0u, 0u, 0u, 0u};
+                }
+                acc = mfma32<C::MT>(af, qf[kk], acc);
+            }
+            if ((l & 31) == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t kr = kb0 + qrow_key_of(r, l);
+                    if (kr < (int64_t)L) {
+                        const float sc = C::SCALE ? a->k_scale[kr] : 1.f;
+                        f((uint32_t)kr, qrow_score<C>(acc[r], w, sc));
+                    }
+                }
+            }
+        }
+    }
+};
+
+// Items of a query's candidate slices (prefix offsets in cpre), streamed.
+struct QRowSliceSrc {
+    const Cand *slices;  // [P][capS]
+    const uint32_t *cpre;
+    int P;
+    uint32_t capS;
+    template <class F>
+    __device__ void for_each(F &&f) const
+    {
+        for (int c = 0; c < P; ++c) {
+            const uint32_t n = cpre[c + 1] - cpre[c];
+            const Cand *s = slices + (size_t)c * capS;
+            for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+                const Cand e = s[i];
+                f(e.idx, e.val);
+            }
+        }
+    }
+};
+
+constexpr int QROW_STASH = 16384;  // candidates kept on chip by the single-head select
+
+template <class C>
+__global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
+{
+    constexpr int NT = SEL_THREADS;
+    __shared__ SelectSmemT<QROW_STASH> sm;
+    __shared__ uint32_t cpre[2 * QROW_MAX_SPLITS + 1];
+    __shared__ uint32_t s_ovf;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = blockIdx.x;
+    const uint32_t L = kv_length(a, t);
+    const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+    const int ncell = 2 * a.P;                 // (split, half) slices of the query
+    const uint32_t capH = (uint32_t)a.capS / 2u;
+    int32_t *oi = a.out_idx + (size_t)t * a.k;
+    float *os = a.out_score + (size_t)t * a.k;
+    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += NT) {
+        oi[i] = -1;
+        os[i] = -__builtin_inff();
+    }
+    if (need == 0) {
+        if (tid == 0 && a.route) a.route[t] = 4;
+        return;
+    }
+    // slice counts -> prefix (cpre) and overflow flag
+    if (tid == 0) s_ovf = 0;
+    __syncthreads();
+    const uint32_t *cnt = a.qcnt + (size_t)t * ncell;
+    if (tid < 64) {
+        uint32_t carry = 0;
+        for (int base = 0; base < ncell; base += 64) {
+            const int c = base + lane;
+            const uint32_t raw = c < ncell ? cnt[c] : 0u;
+            if (raw > capH) atomicOr(&s_ovf, 1u);
+            const uint32_t incl = wave_incl_sum(min(raw, capH));
+            if (c < ncell) cpre[c + 1] = carry + incl;
+            carry += lane_value(incl, 63);
+        }
+        if (tid == 0) cpre[0] = 0;
+    }
+    __syncthreads();
+    const uint32_t n = cpre[ncell];
+    const bool recover = a.force == 1 || s_ovf || n < need;
+    auto emit = [&](uint32_t slot, uint64_t K) {
+        if (slot < need) {
+            oi[slot] = (int32_t)key_index(K);
+            os[slot] = key_value(K);
+        }
+    };
+    if (!recover && n <= (uint32_t)QROW_STASH) {
+        constexpr int B = 8;
+        for (int c = wave; c < ncell; c += NT / 64) {
+            const uint32_t lo = cpre[c], cn = cpre[c + 1] - lo;
+            const Cand *cell = a.cand + ((size_t)t * ncell + c) * capH;
+            for (uint32_t i0 = 0; i0 < cn; i0 += 64 * B) {
+                Cand e[B];
+#pragma unroll
+                for (int j = 0; j < B; ++j) {
+                    const uint32_t i = i0 + j * 64 + lane;
+                    if (i < cn) e[j] = cell[i];
+                }
+#pragma unroll
+                for (int j = 0; j < B; ++j) {
+                    const uint32_t i = i0 + j * 64 + lane;
+                    if (i < cn) sm.stash[lo + i] = make_key(e[j].val, e[j].idx);
+                }
+            }
+        }
+        __syncthreads();
+        select_stashed<NT>(sm, n, need, emit);
+    } else if (!recover) {
+        QRowSliceSrc src{a.cand + (size_t)t * ncell * capH, cpre, ncell, capH};
+        exact_select<NT>(sm, src, need, emit);
+    } else {
+        QRowRescoreSrc<C> src{&a, t, L};
+        exact_select<NT>(sm, src, need, emit);
+    }
+    if (tid == 0 && a.route) a.route[t] = recover ? 3 : 1;
+}
+
+// --------------------------------------------------------------- launch
+template <class C>
+hipError_t launch_qrow_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t stream)
+{
+    hipError_t e;
+    {
+        StageTimer st(ST_F_MINMAX, stream);
+        hipLaunchKernelGGL(k_qrow_sample<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), 0, stream, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        StageTimer st(ST_F_HIST, stream);
+        hipLaunchKernelGGL(k_qrow_gate<C>, dim3(p.T), dim3(SEL_THREADS), 0, stream, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        StageTimer st(ST_F_MAIN, stream);
+        hipLaunchKernelGGL(k_qrow_main<C>, dim3(p.G * p.P), dim3(FUSED_THREADS), 0, stream, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        StageTimer st(ST_F_SELECT, stream);
+        hipLaunchKernelGGL(k_qrow_select<C>, dim3(p.T), dim3(SEL_THREADS), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+FusedLauncher find_qrow_launcher(int qt, int kt, int d, bool relu);
+
+#define ITK_QROW_CASES_FOR(QT, KT)                                                                       \
+    if (qt == QT && kt == KT) {                                                                          \
+        if (d == 64) return relu ? &launch_qrow_cfg<FCfg<QT, KT, 1, 64, true>>                           \
+                                 : &launch_qrow_cfg<FCfg<QT, KT, 1, 64, false>>;                         \
+        if (d == 128) return relu ? &launch_qrow_cfg<FCfg<QT, KT, 1, 128, true>>                         \
+                                  : &launch_qrow_cfg<FCfg<QT, KT, 1, 128, false>>;                       \
+        if (d == 256) return relu ? &launch_qrow_cfg<FCfg<QT, KT, 1, 256, true>>                         \
+                                  : &launch_qrow_cfg<FCfg<QT, KT, 1, 256, false>>;                       \
+    }
+
+}  // namespace itk

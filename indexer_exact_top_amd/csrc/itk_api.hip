@@ -4,7 +4,7 @@
 #include <mutex>
 #include <vector>
 
-#include "fused_impl.hpp"
+#include "fused_qrow.hpp"
 #include "itk_internal.hpp"
 
 namespace itk {
@@ -24,6 +24,16 @@ RouteSink &route_sink()
 FusedLauncher find_fused_launcher_bf16(int, int, int, int, bool);
 FusedLauncher find_fused_launcher_f16(int, int, int, int, bool);
 FusedLauncher find_fused_launcher_f32(int, int, int, int, bool);
+
+FusedLauncher find_qrow_launcher_bf16(int, int, int, bool);
+FusedLauncher find_qrow_launcher_f16(int, int, int, bool);
+
+FusedLauncher find_qrow_launcher(int qt, int kt, int d, bool relu)
+{
+    if (qt == ITK_BF16) return find_qrow_launcher_bf16(qt, kt, d, relu);
+    if (qt == ITK_F16) return find_qrow_launcher_f16(qt, kt, d, relu);
+    return nullptr;
+}
 
 FusedLauncher find_fused_launcher(int qt, int kt, int hb, int d, bool relu)
 {
@@ -93,6 +103,52 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     const Knobs &kn = knobs();
     FusedPlan p;
     p.T = T; p.H = H; p.D = D; p.N = N; p.k = k; p.qt = qt; p.kt = kt; p.flags = flags; p.HB = HB;
+    if (H == 1 && qt != ITK_F32 && find_qrow_launcher(qt, kt, D, relu)) {
+        // Single head: queries are the MFMA columns (32 per block, 512 per
+        // workgroup); keys are split so that about 256 workgroups run.
+        p.qrow = true;
+        p.G = (int32_t)ceil_div_u((uint64_t)T, 512);
+        const int64_t stage = (D * 2 <= 256) ? 128 : 64;
+        int P = p.G >= 256 ? 1 : (int)ceil_div_u(256, (uint64_t)p.G);
+        if (P >= 8) P = (int)ceil_div_u((uint64_t)P, 8) * 8;
+        const int Pmax = (int)(N / (4 * stage)) > 1 ? (int)(N / (4 * stage)) : 1;
+        if (P > Pmax) P = Pmax;
+        if (kn.splits > 0) P = kn.splits;
+        if (P > QROW_MAX_SPLITS) P = QROW_MAX_SPLITS;
+        int64_t span = (int64_t)ceil_div_u((uint64_t)N, (uint64_t)P);
+        span = (int64_t)ceil_div_u((uint64_t)span, (uint64_t)stage) * stage;
+        P = (int)ceil_div_u((uint64_t)N, (uint64_t)span);
+        p.P = P; p.span = span;
+        p.Ps = P; p.span_s = span;
+        p.rho = kn.rho > 0.f ? kn.rho : 2.0f;
+        // view: about 8 rho k sampled keys per query (between 4096 and 32768)
+        double want = 8.0 * p.rho * k;
+        if (want < 4096.0) want = 4096.0;
+        if (want > 32768.0) want = 32768.0;
+        const int64_t ntiles = (int64_t)ceil_div_u((uint64_t)N, TILE_KEYS);
+        int64_t st = (int64_t)ceil((double)N / want);
+        if (st < 1) st = 1;
+        if (st > 4096) st = 4096;
+        if (kn.sample_stride > 0) st = kn.sample_stride;
+        p.sample_tiles = (int32_t)st;
+        p.samp_cap = (int64_t)ceil_div_u((uint64_t)ntiles, (uint64_t)st) * TILE_KEYS;
+        // per-(query, split) capacity: 4x the expected share of rho k, >= 64
+        int64_t capS = (int64_t)ceil(4.0 * p.rho * k / P);
+        if (kn.capacity > 0) capS = (int64_t)ceil_div_u((uint64_t)kn.capacity, (uint64_t)P);
+        if (capS < 128) capS = 128;
+        capS = (capS + 127) / 128 * 128;  // two halves of a multiple of 64
+        p.capS = (int32_t)capS;
+        p.cap = (int32_t)(capS * P);
+        p.force = kn.force_route;
+        size_t off = 0;
+        p.off_samp = off; off = align256(off + (size_t)T * p.samp_cap * sizeof(float));
+        p.off_gate = off; off = align256(off + (size_t)T * sizeof(float));
+        p.off_qcnt = off; off = align256(off + (size_t)T * P * 2 * sizeof(uint32_t));
+        p.off_cand = off; off = align256(off + (size_t)T * P * capS * sizeof(Cand));
+        p.bytes = off;
+        *out = p;
+        return ITK_OK;
+    }
     p.G = (int32_t)ceil_div_u((uint64_t)T, FUSED_WAVES);
     // Key splits: fill the 256 CUs with about one workgroup each; a split
     // count that is a multiple of 8 places each split on one XCD.
@@ -148,6 +204,18 @@ hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const 
     a.N = p.N; a.span = p.span; a.span_s = p.span_s;
     a.T = p.T; a.H = p.H; a.k = p.k; a.cap = p.cap; a.G = p.G; a.P = p.P; a.Ps = p.Ps;
     a.sample_tiles = p.sample_tiles; a.force = p.force; a.rho = p.rho;
+    a.samp = nullptr; a.gate = nullptr; a.qcnt = nullptr; a.samp_cap = 0; a.capS = 0;
+    if (p.qrow) {
+        a.samp = reinterpret_cast<float *>(w + p.off_samp);
+        a.gate = reinterpret_cast<float *>(w + p.off_gate);
+        a.qcnt = reinterpret_cast<uint32_t *>(w + p.off_qcnt);
+        a.cand = reinterpret_cast<Cand *>(w + p.off_cand);
+        a.samp_cap = p.samp_cap;
+        a.capS = p.capS;
+        FusedLauncher fn = find_qrow_launcher(p.qt, p.kt, p.D, !(p.flags & ITK_FLAG_NO_RELU));
+        if (!fn) return hipErrorInvalidValue;
+        return fn(p, a, stream);
+    }
     FusedLauncher fn = find_fused_launcher(p.qt, p.kt, p.HB, p.D, !(p.flags & ITK_FLAG_NO_RELU));
     if (!fn) return hipErrorInvalidValue;
     return fn(p, a, stream);

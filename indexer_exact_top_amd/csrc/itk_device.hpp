@@ -253,9 +253,12 @@ __device__ void find_boundary(const uint32_t *hist, uint32_t quota, uint32_t *sc
 }
 
 // --------------------------------------------------------- exact select
-struct SelectSmem {
+// LDS of one selecting workgroup; CAP composite keys fit on chip.
+template <int CAP>
+struct SelectSmemT {
+    static constexpr int cap = CAP;
     uint32_t hist[NBINS];
-    uint64_t stash[STASH_CAP];
+    uint64_t stash[CAP];
     uint64_t bound[BOUND_CAP];
     float vmin[16], vmax[16];
     uint32_t n_bound;
@@ -266,6 +269,7 @@ struct SelectSmem {
     BoundaryOut b;
     uint32_t scan[16];
 };
+using SelectSmem = SelectSmemT<STASH_CAP>;
 
 // Exact Top-`need` of the items produced by `src` under the composite key.
 //
@@ -280,8 +284,8 @@ struct SelectSmem {
 // the boundary digit, commit strictly better digits, retain the boundary
 // group.  As soon as the boundary group fits STASH_CAP it is copied on chip
 // (and everything above it emitted) so that later rounds never touch `src`.
-template <int NT, class Src, class Emit>
-__device__ void exact_select(SelectSmem &sm, Src &src, uint32_t need, Emit &&emit, int prestashed = -1)
+template <int NT, class SM, class Src, class Emit>
+__device__ void exact_select(SM &sm, Src &src, uint32_t need, Emit &&emit, int prestashed = -1)
 {
     const int tid = threadIdx.x;
     if (tid == 0) {
@@ -342,7 +346,7 @@ __device__ void exact_select(SelectSmem &sm, Src &src, uint32_t need, Emit &&emi
             __syncthreads();
             return;
         }
-        if (!sm.stashed && sm.b.eq <= (uint32_t)STASH_CAP) {
+        if (!sm.stashed && sm.b.eq <= (uint32_t)SM::cap) {
             src.for_each([&](uint32_t idx, float v) {
                 const uint64_t K = make_key(v, idx);
                 const uint64_t km = K & M2;
@@ -351,7 +355,7 @@ __device__ void exact_select(SelectSmem &sm, Src &src, uint32_t need, Emit &&emi
                 const uint32_t slot = wave_reserve(above, &sm.out_n);
                 if (above) emit(slot, K);
                 const uint32_t s = wave_reserve(keep, &sm.stash_n);
-                if (keep && s < (uint32_t)STASH_CAP) sm.stash[s] = K;
+                if (keep && s < (uint32_t)SM::cap) sm.stash[s] = K;
             });
             __syncthreads();
             if (tid == 0) sm.stashed = 1u;
@@ -367,7 +371,7 @@ struct NoSrc {
 };
 
 // Exact Top-`need` of the `n` items whose composite keys the caller has put
-// into sm.stash (n <= STASH_CAP, 1 <= need <= n, followed by a barrier).
+// into sm.stash (n <= SM::cap, 1 <= need <= n, followed by a barrier).
 //
 // A value histogram first narrows the problem: NBINS equal-width bins over
 // the items' own [min, max] (a monotone map of the value, so the order of
@@ -378,8 +382,8 @@ struct NoSrc {
 // boundary including the lower-index rule for equal values.  When the range
 // is degenerate or the boundary bin is too large to gather, the radix rounds
 // run over all n items instead.
-template <int NT, class Emit>
-__device__ void select_stashed(SelectSmem &sm, uint32_t n, uint32_t need, Emit &&emit)
+template <int NT, class SM, class Emit>
+__device__ void select_stashed(SM &sm, uint32_t n, uint32_t need, Emit &&emit)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     NoSrc nosrc;

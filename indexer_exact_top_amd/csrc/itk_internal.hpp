@@ -62,6 +62,7 @@ constexpr int FUSED_WAVES = 8;                  // queries per workgroup
 constexpr int FUSED_THREADS = FUSED_WAVES * 64;
 constexpr int TILE_KEYS = 64;
 constexpr int SEL_THREADS = 512;   // fused select: one workgroup per row
+constexpr int QROW_MAX_SPLITS = 256;  // single-head path: key splits per query
 
 struct FusedPlan {
     int32_t T = 0, H = 0, D = 0, k = 0;
@@ -78,7 +79,11 @@ struct FusedPlan {
     float rho = 2.0f;
     int32_t cap = 0;         // candidates per row
     int32_t force = 0;
-    size_t off_param = 0, off_mm = 0, off_hist = 0, off_tail = 0, off_gate = 0, off_cand = 0, bytes = 0;
+    bool qrow = false;       // single-head path: queries as MFMA columns
+    int32_t capS = 0;        // single head: candidates per (query, key split)
+    int64_t samp_cap = 0;    // single head: stored view scores per query
+    size_t off_param = 0, off_mm = 0, off_hist = 0, off_tail = 0, off_gate = 0, off_cand = 0;
+    size_t off_samp = 0, off_qcnt = 0, bytes = 0;
 };
 itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk_dtype qt, itk_dtype kt,
                       uint32_t flags, FusedPlan *out);

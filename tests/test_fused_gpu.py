@@ -103,3 +103,39 @@ def test_config4_sampled_rows(itk):
     idx, sc, routes = _run(itk, case, routes=True)
     rec = check_fused_rows(case, [0, 9], idx, sc, min_recall=0.95)
     print(f"config4 (T=16) recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
+
+
+@pytest.mark.parametrize("knobs", [dict(force_route=1), dict(capacity=1024, rho=50.0), dict(splits=8),
+                                   dict(sample_stride=1, rho=1.0), dict(splits=3, sample_stride=5)])
+@pytest.mark.parametrize("qt,relu", [(synth.F16, False), (synth.BF16, True)])
+def test_single_head_routes_and_plans_give_identical_sets(itk, knobs, qt, relu):
+    # 600 queries: two 512-query groups, the second ragged; lengths vary.
+    T = 600
+    kv = (np.arange(T) * 37 % 50000 + 9000).astype(np.int32)
+    kv[:5] = [60000, 1, 0, 700, 699]
+    case = synth.gen_fused(T, 1, 128, 60000, 700, q_dtype=qt, k_dtype=qt, kv_len=kv, no_relu=not relu,
+                           unit_norm=not relu, seed=61 + relu)
+    base, bsc, _ = _run(itk, case)
+    itk.set_plan_opts(**knobs)
+    got, gsc, routes = _run(itk, case, routes=True)
+    print(knobs, "routes", np.bincount(routes).tolist())
+    check_fused_rows(case, [0, 1, 2, 3, 4, 5, 300, 511, 512, 599], got, gsc, min_recall=0.95)
+    assert np.array_equal(np.sort(base, axis=1), np.sort(got, axis=1))
+
+
+# Full-size workloads in the launch configuration the benchmark times
+# (default plan); the oracle checks sampled rows one by one.
+@pytest.mark.parametrize("cfg,rows,min_recall", [(3, [0, 1023, 2047], 0.99), (4, [0, 127], 0.95),
+                                                 (5, [0, 511, 1023], 0.99)])
+def test_full_size_sampled_rows(itk, cfg, rows, min_recall):
+    case = synth.fused_config(cfg)
+    idx, sc, routes = _run(itk, case, routes=True)
+    rec = check_fused_rows(case, rows, idx, sc, min_recall=min_recall)
+    # invariants on every row: |out| = min(k, L), distinct, in range
+    need = np.minimum(case.k, case.kv_len)
+    for t in range(case.T):
+        sel = idx[t, :need[t]]
+        assert (idx[t, need[t]:] == -1).all()
+        assert ((sel >= 0) & (sel < case.kv_len[t])).all()
+        assert np.unique(sel).size == need[t]
+    print(f"config{cfg} full size: recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
