@@ -379,39 +379,29 @@ __device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int
 
 // ---------------------------------------------------- tile staging (LDS)
 // Double-buffered key stages (and the per-key scales of FP8 keys).
-template <class C, int NB = 2>
+template <class C>
 struct TileBuf {
-    static constexpr int nbuf = NB;
-    char k[NB][C::STAGE_BYTES];
-    char sink[1024];            // target of the padding copies (never read)
-    float scale[2][TILE_KEYS];  // FP8 keys (register staging, two buffers)
+    char k[2][C::STAGE_BYTES];
+    float scale[2][TILE_KEYS];
 };
 
-// s_waitcnt vmcnt(N) (other counters untouched).
-template <int N>
-__device__ __forceinline__ void wait_vmem_le()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // One wave instruction of the direct global -> LDS copy: lane i's 16 bytes
-// at `src` land at LDS byte lds_base + 16 i (lds_base is wave-uniform and
-// goes through M0, which is restored afterwards).  Issued from inline
-// assembly so that the compiler does not fence later LDS accesses of other
-// buffers on it; the caller waits for completion (vmcnt) before the barrier
-// that publishes the stage.
-__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base)
+// at byte `voff` from the wave-uniform address `sbase` land at LDS byte
+// lds_base + 16 i (lds_base is wave-uniform and goes through M0, which is
+// restored afterwards).  Issued from inline assembly so that the compiler
+// does not fence later LDS accesses of other buffers on it; the caller waits
+// for completion (vmcnt) before the barrier that publishes the stage.
+__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint32_t lds_base)
 {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(src), "s"(lds_base)
+        : "v"(voff), "s"(sbase), "s"(lds_base)
         : "memory");
 }
 
@@ -433,8 +423,8 @@ struct DmaPlan {
     static constexpr int PIECES = NSUB * TILE_KEYS * C::SPR / 64;
     static constexpr int PER_WAVE = (PIECES + FUSED_WAVES - 1) / FUSED_WAVES;
     static_assert(PIECES * 64 == NSUB * TILE_KEYS * C::SPR, "stage must split into 1 KB pieces");
-    int src_off[PER_WAVE];  // row * ROWB + chunk * 16
-    int row[PER_WAVE];
+    static_assert((C::ROWB & (C::ROWB - 1)) == 0, "key rows are a power of two bytes");
+    uint32_t src_off[PER_WAVE];  // row * ROWB + chunk * 16, from the stage's first key
 
     __device__ void init()
     {
@@ -443,32 +433,29 @@ struct DmaPlan {
         for (int j = 0; j < PER_WAVE; ++j) {
             const int q = (j * FUSED_WAVES + wave) * 64 + lane;
             const int r = q / C::SPR, c = q % C::SPR;
-            row[j] = r;
-            src_off[j] = r * C::ROWB + (c < C::CH ? c : 0) * 16;
+            src_off[j] = (uint32_t)(r * C::ROWB + (c < C::CH ? c : 0) * 16);
         }
     }
 
-    // With more than two stage buffers every wave issues exactly PER_WAVE copy
-    // instructions per stage (pieces past the stage re-copy the first key row
-    // into tb.sink), so that a wave's count of copies in flight is a
-    // compile-time multiple of PER_WAVE.
-    template <int NB>
-    __device__ __forceinline__ void issue(const FusedArgs &a, TileBuf<C, NB> &tb, int buf, int64_t key0) const
+    // Copies the stage starting at key0 into buffer `buf`.  Rows at or past
+    // key N re-read the same chunk of the last key (never read back).
+    __device__ __forceinline__ void issue(const FusedArgs &a, TileBuf<C> &tb, int buf, int64_t key0) const
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const uint32_t base = lds_addr(tb.k[buf]);
         const char *kbase = static_cast<const char *>(a.K) + (size_t)key0 * C::ROWB;
         const bool tail = key0 + NSUB * TILE_KEYS > a.N;
+        const uint32_t last_row = (uint32_t)(a.N - 1 - key0);  // key0 < N
 #pragma unroll
         for (int j = 0; j < PER_WAVE; ++j) {
             const int piece = j * FUSED_WAVES + wave;
             if (piece < PIECES) {
-                const char *src = kbase + src_off[j];
-                if (tail && key0 + row[j] >= a.N)
-                    src = static_cast<const char *>(a.K) + (size_t)(a.N - 1) * C::ROWB + (src_off[j] - row[j] * C::ROWB);
-                lds_dma16(src, base + (uint32_t)piece * 1024u);
-            } else if constexpr (NB > 2) {
-                lds_dma16(static_cast<const char *>(a.K) + (threadIdx.x & 63) * 16 % C::ROWB, lds_addr(tb.sink));
+                uint32_t off = src_off[j];
+                if (tail) {
+                    const uint32_t r = off / C::ROWB;
+                    off = (r < last_row ? r : last_row) * C::ROWB + (off & (C::ROWB - 1));
+                }
+                lds_dma16(kbase, off, base + (uint32_t)piece * 1024u);
             }
         }
     }

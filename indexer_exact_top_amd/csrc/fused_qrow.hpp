@@ -33,6 +33,22 @@ constexpr int QROW_QB = 2;                      // 32-query blocks per wave
 constexpr int QROW_QPW = 32 * QROW_QB;          // queries per wave
 constexpr int QROW_Q = QROW_QPW * FUSED_WAVES;  // queries per workgroup
 
+// Without ReLU a score w * (q . k) is computed as |w| * ((sign(w) q) . k):
+// negating the 16-bit query operands negates every product and partial sum
+// exactly (round-to-nearest-even is symmetric), so the score is the same up to
+// the sign of a zero (which the selection key ignores), and it becomes a
+// non-decreasing function of the accumulator.  With ReLU nothing is folded.
+template <class C>
+__device__ __forceinline__ uint32_t qrow_qsign(float w)
+{
+    return (!C::RELU && (__float_as_uint(w) >> 31)) ? 0x80008000u : 0u;
+}
+template <class C>
+__device__ __forceinline__ float qrow_weight(float w)
+{
+    return C::RELU ? w : __builtin_fabsf(w);
+}
+
 // Per-lane query state: lane l owns query column l % 32 of every block.
 template <class C>
 struct QRowQ {
@@ -48,13 +64,16 @@ struct QRowQ {
         for (int qb = 0; qb < QROW_QB; ++qb) {
             t[qb] = g * QROW_Q + wave * QROW_QPW + qb * 32 + (l & 31);
             const bool act = t[qb] < a.T;
-            w[qb] = act ? a.W[t[qb]] : 0.f;
+            const float wr = act ? a.W[t[qb]] : 0.f;
+            const uint32_t sg = qrow_qsign<C>(wr);
+            w[qb] = qrow_weight<C>(wr);
             L[qb] = act ? kv_length(a, t[qb]) : 0u;
 #pragma unroll
             for (int kk = 0; kk < C::KS; ++kk) {
                 const int d0 = kk * 16 + 8 * (l >> 5);
                 const char *ptr = static_cast<const char *>(a.Q) + ((size_t)(act ? t[qb] : 0) * C::D + d0) * 2;
-                q[qb][kk] = act ? *reinterpret_cast<const u32x4_t *>(ptr) : u32x4_t{0u, 0u, 0u, 0u};
+                const u32x4_t v = act ? *reinterpret_cast<const u32x4_t *>(ptr) : u32x4_t{0u, 0u, 0u, 0u};
+                q[qb][kk] = u32x4_t{v[0] ^ sg, v[1] ^ sg, v[2] ^ sg, v[3] ^ sg};
             }
         }
     }
@@ -121,59 +140,39 @@ __device__ __forceinline__ void qrow_block_scales(float (&sc)[16], const float *
     }
 }
 
-// Stage buffers of the QRow scan (16-/32-bit keys; FP8 keys go through
-// registers with two buffers).  Deeper copy pipelines (4 buffers, 3 stages in
-// flight) measured no faster on 4M x 256 fp16 keys.
-constexpr int QROW_NB = 2;
-template <class C>
-using QRowTiles = TileBuf<C, C::DMA ? QROW_NB : 2>;
-
-// Waits until at most `n_after` stages' copies of this wave are in flight.
-template <int PW, int NB>
-__device__ __forceinline__ void wait_stages_after(int n_after)
-{
-    static_assert(NB <= 4, "wait table");
-    if (n_after <= 0) wait_vmem_le<0>();
-    else if (n_after == 1) wait_vmem_le<PW>();
-    else wait_vmem_le<2 * PW>();
-}
-
 // The pipelined QRow scan: `nstages` stages of NSUB 64-key tiles, the first
 // at key `first`, `step` keys apart, keys at or beyond `key_end` skipped.
 // visit(kb0, acc, sc) is called once per computed 32-key block (wave-uniform)
 // with the block's first key and the accumulators (and FP8 scales).  Every
 // thread of the workgroup must call this.
 template <class C, int NSUB, class Visit>
-__device__ __forceinline__ void qrow_scan(const FusedArgs &a, QRowTiles<C> &tb, const QRowQ<C> &qq, int64_t first,
+__device__ __forceinline__ void qrow_scan(const FusedArgs &a, TileBuf<C> &tb, const QRowQ<C> &qq, int64_t first,
                                           int64_t step, int nstages, int64_t key_end, uint32_t wave_maxL,
                                           Visit &&visit)
 {
     static_assert(C::DMA || NSUB == 1, "FP8 staging moves one 64-key tile per stage");
-    constexpr int NB = QRowTiles<C>::nbuf;
-    constexpr int PW = DmaPlan<C, NSUB>::PER_WAVE;
     const int64_t kend = key_end < (int64_t)wave_maxL ? key_end : (int64_t)wave_maxL;
     KStage<C> ks;
     DmaPlan<C, NSUB> dp;
     if constexpr (C::DMA) dp.init();
-    const int pre = nstages < NB - 1 ? nstages : NB - 1;  // stages in flight before the loop
-    if constexpr (C::DMA) {
-        for (int s0 = 0; s0 < pre; ++s0) dp.issue(a, tb, s0, first + (int64_t)s0 * step);
-    } else if (nstages > 0) {
-        ks.load(a, first);
-        ks.store(tb, 0);
+    if (nstages > 0) {
+        if constexpr (C::DMA) {
+            dp.issue(a, tb, 0, first);
+        } else {
+            ks.load(a, first);
+            ks.store(tb, 0);
+        }
     }
     const_cast<QRowQ<C> &>(qq).settle();
-    if constexpr (C::DMA) wait_stages_after<PW, NB>(pre - 1);
-    else wait_vmem_all();
+    wait_vmem_all();
     __syncthreads();
     const int boff = bfrag_lane_off<C>();
     for (int st = 0; st < nstages; ++st) {
         const int64_t skey = first + (int64_t)st * step;
-        const int buf = st % NB;
-        if constexpr (C::DMA) {
-            if (st + NB - 1 < nstages) dp.issue(a, tb, (st + NB - 1) % NB, skey + (int64_t)(NB - 1) * step);
-        } else if (st + 1 < nstages) {
-            ks.load(a, skey + step);
+        const int buf = st & 1;
+        if (st + 1 < nstages) {
+            if constexpr (C::DMA) dp.issue(a, tb, buf ^ 1, skey + step);
+            else ks.load(a, skey + step);
         }
 #pragma unroll
         for (int blk = 0; blk < 2 * NSUB; ++blk) {
@@ -187,14 +186,8 @@ __device__ __forceinline__ void qrow_scan(const FusedArgs &a, QRowTiles<C> &tb, 
             }
         }
         if (st + 1 < nstages) {
-            if constexpr (C::DMA) {
-                // stage st+1 complete; stages st+2 .. issued may stay in flight
-                const int last_issued = (st + NB - 1 < nstages ? st + NB - 1 : nstages - 1);
-                wait_stages_after<PW, NB>(last_issued - (st + 1));
-            } else {
-                ks.store(tb, buf ^ 1);
-                wait_vmem_all();
-            }
+            if constexpr (!C::DMA) ks.store(tb, buf ^ 1);
+            wait_vmem_all();
         }
         __syncthreads();
     }
@@ -215,7 +208,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_sample(FusedArgs a)
 {
-    __shared__ QRowTiles<C> tb;
+    __shared__ TileBuf<C> tb;
     const int l = (int)lane_id();
     int g, p;
     map_group_split(blockIdx.x, a.G, a.Ps, g, p);
@@ -330,17 +323,83 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_gate(FusedArgs a)
 }
 
 // ------------------------------------------------ scan: gate and collect
+// A value no larger than any accumulator whose score (qrow_score without
+// per-key scales, weight w after folding) can reach `gate`: the scan tests the
+// accumulator against it and computes the exact score only for the few that
+// are not below it.  Scores are non-decreasing in the accumulator for w >= 0;
+// for w < 0 (ReLU only) every accumulator is tested exactly.
+__device__ __forceinline__ float qrow_acc_floor(float gate, float w, bool relu)
+{
+    const float ninf = -__builtin_inff();
+    if (!(gate > ninf)) return ninf;
+    if (w != w) return __builtin_nanf("");  // every score is NaN: nothing passes
+    if (w < 0.f) return ninf;
+    if (w == 0.f) return gate <= 0.f ? ninf : __builtin_inff();
+    if (relu && gate <= 0.f) return ninf;
+    // x * w >= gate (rounded) needs x >= gate / w up to about one ulp of each
+    // rounding; 8 ulps below the quotient is safely below that.
+    const float x = gate / w;
+    if (x != x) return ninf;
+    uint32_t u = __float_as_uint(x);
+    uint32_t o = (u >> 31) ? ~u : (u | 0x80000000u);  // ascending order
+    const uint32_t o_ninf = 0x007FFFFFu;               // order key of -inf
+    o = o > o_ninf + 8u ? o - 8u : o_ninf;
+    u = (o >> 31) ? (o & 0x7FFFFFFFu) : ~o;
+    return __uint_as_float(u);
+}
+
+// Appends every score of a 32-key block that is at or above the lane's gate
+// to the lane's half of its (query, split) slice.  A block almost never has
+// a passing score in a given accumulator register across the whole wave, so
+// each register costs one multiply, one compare and one wave-uniform branch.
+// Past the slice capacity the last slot is overwritten: the count still
+// grows, and a count above the capacity sends the query to recovery.
+template <class C, bool PARTIAL>
+__device__ __forceinline__ void qrow_collect(const f32x16_t (&acc)[QROW_QB], const float (&sc)[16],
+                                             const QRowQ<C> &qq, const float (&gate)[QROW_QB],
+                                             const float (&afloor)[QROW_QB],
+                                             const int64_t (&kend)[QROW_QB], int64_t kb0, Cand *const (&slice)[QROW_QB],
+                                             uint32_t (&cnt)[QROW_QB], uint32_t capH)
+{
+    const int l = (int)lane_id();
+    const uint32_t kb = (uint32_t)kb0 + 4u * (uint32_t)(l >> 5);  // key of register 0
+    int32_t lim[QROW_QB];  // valid rows of the block (PARTIAL only): row < lim
+#pragma unroll
+    for (int qb = 0; qb < QROW_QB; ++qb) {
+        const int64_t d = kend[qb] - kb0;
+        lim[qb] = d < 0 ? 0 : (d > 32 ? 32 : (int32_t)d);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QROW_QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            bool maybe;
+            if constexpr (C::SCALE) maybe = true;
+            else maybe = acc[qb][r] >= afloor[qb];
+            if (maybe) {
+                const float s = qrow_score<C>(acc[qb][r], qq.w[qb], sc[r]);
+                bool pass = s >= gate[qb];
+                if constexpr (PARTIAL) pass = pass && qrow_key_of(r, l) < lim[qb];
+                if (pass) {
+                    const uint32_t slot = cnt[qb] < capH ? cnt[qb] : capH - 1u;
+                    slice[qb][slot] = Cand{kb + (uint32_t)(8 * (r >> 2) + (r & 3)), s};
+                    ++cnt[qb];
+                }
+            }
+        }
+}
+
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_main(FusedArgs a)
 {
-    __shared__ QRowTiles<C> tb;
+    __shared__ TileBuf<C> tb;
     const int tid = threadIdx.x, l = tid & 63;
     int g, p;
     map_group_split(blockIdx.x, a.G, a.P, g, p);
     if (a.force == 1) return;  // every query takes the re-scoring route
     QRowQ<C> qq;
     qq.load(a, g);
-    float gate[QROW_QB];
+    float gate[QROW_QB], afloor[QROW_QB];
     int64_t kend[QROW_QB];
     const int64_t k_lo = (int64_t)p * a.span;
     int64_t k_hi = k_lo + a.span;
@@ -349,6 +408,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_main(FusedArgs a)
     for (int qb = 0; qb < QROW_QB; ++qb) {
         const bool act = qq.t[qb] < a.T;
         gate[qb] = act ? a.gate[qq.t[qb]] : __builtin_inff();
+        afloor[qb] = qrow_acc_floor(gate[qb], qq.w[qb], C::RELU);
         kend[qb] = (int64_t)qq.L[qb] < k_hi ? (int64_t)qq.L[qb] : k_hi;
         wmax = max(wmax, qq.L[qb]);
     }
@@ -383,27 +443,12 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_main(FusedArgs a)
 
     qrow_scan<C, C::NSUB>(a, tb, qq, k_lo, C::STAGE_KEYS, nstages, k_hi, gmaxL,
                           [&](int64_t kb0, const f32x16_t (&acc)[QROW_QB], const float (&sc)[16]) {
-                              const bool full = kb0 + 32 <= k_lo + (int64_t)kmin;
-                              // valid key rows of this block per query block: row < lim
-                              int32_t lim[QROW_QB];
-#pragma unroll
-                              for (int qb = 0; qb < QROW_QB; ++qb) {
-                                  const int64_t d = kend[qb] - kb0;
-                                  lim[qb] = d < 0 ? 0 : (d > 32 ? 32 : (int32_t)d);
-                              }
-#pragma unroll
-                              for (int qb = 0; qb < QROW_QB; ++qb) {
-#pragma unroll
-                                  for (int r = 0; r < 16; ++r) {
-                                      const float s = qrow_score<C>(acc[qb][r], qq.w[qb], sc[r]);
-                                      const int kr = qrow_key_of(r, l);
-                                      const bool pass = s >= gate[qb] && (full || kr < lim[qb]);
-                                      if (pass) {
-                                          if (cnt[qb] < capH) myslice[qb][cnt[qb]] = Cand{(uint32_t)kb0 + (uint32_t)kr, s};
-                                          ++cnt[qb];
-                                      }
-                                  }
-                              }
+                              // Block entirely below every query's length: no
+                              // per-key validity test (wave-uniform choice).
+                              if (kb0 + 32 <= k_lo + (int64_t)kmin)
+                                  qrow_collect<C, false>(acc, sc, qq, gate, afloor, kend, kb0, myslice, cnt, capH);
+                              else
+                                  qrow_collect<C, true>(acc, sc, qq, gate, afloor, kend, kb0, myslice, cnt, capH);
                           });
 #pragma unroll
     for (int qb = 0; qb < QROW_QB; ++qb)
@@ -424,14 +469,17 @@ struct QRowRescoreSrc {
     {
         const int l = (int)lane_id();
         const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-        const float w = a->W[t];
+        const float wr = a->W[t];
+        const uint32_t sg = qrow_qsign<C>(wr);
+        const float w = qrow_weight<C>(wr);
         typename C::frag qf[C::KS];
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) {
             const int d0 = kk * 16 + 8 * (l >> 5);
-            qf[kk] = (l & 31) == 0 ? *reinterpret_cast<const u32x4_t *>(static_cast<const char *>(a->Q) +
-                                                                          ((size_t)t * C::D + d0) * 2)
-                                   : u32x4_t{0u, 0u, 0u, 0u};
+            const u32x4_t v = (l & 31) == 0 ? *reinterpret_cast<const u32x4_t *>(static_cast<const char *>(a->Q) +
+                                                                                 ((size_t)t * C::D + d0) * 2)
+                                            : u32x4_t{0u, 0u, 0u, 0u};
+            qf[kk] = u32x4_t{v[0] ^ sg, v[1] ^ sg, v[2] ^ sg, v[3] ^ sg};
         }
         for (int64_t kb0 = (int64_t)wave * 32; kb0 < (int64_t)L; kb0 += (int64_t)nw * 32) {
             const int64_t key = kb0 + (l & 31);

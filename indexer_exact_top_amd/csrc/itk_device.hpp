@@ -22,7 +22,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int NBINS = 2048;       // one 2^11-bin histogram, reused by every round
 constexpr int STASH_CAP = 7680;   // items kept on chip (60 KB of composite keys)
-constexpr int BOUND_CAP = 1024;   // boundary-bin items kept for the final exact rounds
+constexpr int BOUND_CAP = 1024;
+constexpr int RANK_CAP = 128;     // boundary bins up to this size are settled by ranking   // boundary-bin items kept for the final exact rounds
 
 // ----------------------------------------------------------------- keys
 // Order-preserving map fp32 -> u32 (larger value -> larger key).  -0 is
@@ -383,39 +384,39 @@ struct NoSrc {
 // is degenerate or the boundary bin is too large to gather, the radix rounds
 // run over all n items instead.
 template <int NT, class SM, class Emit>
-__device__ void select_stashed(SM &sm, uint32_t n, uint32_t need, Emit &&emit)
+__device__ void select_stashed(SM &sm, uint32_t n, uint32_t need, Emit &&emit, bool range_ready = false)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     NoSrc nosrc;
-    // value range
     // every loop below reads its LDS items in batches of SB per thread, so
     // that a thread waits for one LDS round trip per batch, not per item
     constexpr int SB = 4;
-    float mn = __builtin_inff(), mx = -__builtin_inff();
-    for (uint32_t i0 = tid; i0 < n; i0 += SB * NT) {
-        float v[SB];
+    if (!range_ready) {  // value range (else each wave's was stored while gathering)
+        float mn = __builtin_inff(), mx = -__builtin_inff();
+        for (uint32_t i0 = tid; i0 < n; i0 += SB * NT) {
+            float v[SB];
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-            const uint32_t i = i0 + j * NT;
-            v[j] = i < n ? key_value(sm.stash[i]) : __builtin_nanf("");
-        }
+            for (int j = 0; j < SB; ++j) {
+                const uint32_t i = i0 + j * NT;
+                v[j] = i < n ? key_value(sm.stash[i]) : __builtin_nanf("");
+            }
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-            mn = fminf(mn, v[j]);  // fminf/fmaxf ignore the NaN padding
-            mx = fmaxf(mx, v[j]);
+            for (int j = 0; j < SB; ++j) {
+                mn = fminf(mn, v[j]);  // fminf/fmaxf ignore the NaN padding
+                mx = fmaxf(mx, v[j]);
+            }
         }
-    }
-    mn = wave_min(mn);
-    mx = wave_max(mx);
-    if (lane == 0) {
-        sm.vmin[wave] = mn;
-        sm.vmax[wave] = mx;
+        mn = wave_min(mn);
+        mx = wave_max(mx);
+        if (lane == 0) {
+            sm.vmin[wave] = mn;
+            sm.vmax[wave] = mx;
+        }
     }
     for (int i = tid; i < NBINS; i += NT) sm.hist[i] = 0u;
     if (tid == 0) sm.n_bound = 0;
     __syncthreads();
-    mn = sm.vmin[0];
-    mx = sm.vmax[0];
+    float mn = sm.vmin[0], mx = sm.vmax[0];
 #pragma unroll
     for (int w = 1; w < NT / 64; ++w) {
         mn = fminf(mn, sm.vmin[w]);
@@ -486,6 +487,19 @@ __device__ void select_stashed(SM &sm, uint32_t n, uint32_t need, Emit &&emit)
     const uint32_t q = need - above;  // 1 <= q <= eq
     if (q == eq) {
         for (uint32_t i = tid; i < eq; i += NT) emit(above + i, sm.bound[i]);
+        __syncthreads();
+        return;
+    }
+    if (eq <= (uint32_t)RANK_CAP) {
+        // A small boundary bin: every item's rank among the bin's items (all
+        // composite keys are distinct) decides it directly; items ranked
+        // below q fill slots above + rank.
+        if ((uint32_t)tid < eq) {
+            const uint64_t K = sm.bound[tid];
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < eq; ++j) rank += sm.bound[j] > K ? 1u : 0u;
+            if (rank < q) emit(above + rank, K);
+        }
         __syncthreads();
         return;
     }

@@ -36,6 +36,14 @@ RouteSink &route_sink();
 // --------------------------------------------------------------- ragged
 constexpr int RAG_THREADS = 256;
 constexpr int RAG_WAVES = RAG_THREADS / 64;
+// Ragged scan: 16-byte loads per thread per batch (two batches in flight),
+// and the longest segment one workgroup scans.
+#ifndef RAG_U
+#define RAG_U 8
+#endif
+#ifndef RAG_SEG_MAX
+#define RAG_SEG_MAX 32768
+#endif
 constexpr int RAG_MAX_CELLS = 64;
 constexpr int FIN_THREADS = 1024;  // ragged finisher: one workgroup per row  // (segment, wave) cells per row whose candidates the finisher gathers on chip
 

@@ -74,6 +74,25 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
     }
     const float *row = a.scores + (size_t)r * (size_t)a.pitch;
 
+    // The segment's first batch of 16-byte loads is issued before phase 1,
+    // so that its memory latency overlaps the view pass; later batches are
+    // double-buffered against the classification of the previous one.
+    constexpr int U = RAG_U;
+    constexpr uint32_t BATCH = (uint32_t)RAG_THREADS * U;  // float4 per batch
+    const uint32_t n4 = (VEC && seg_hi > seg_lo) ? (uint32_t)((seg_hi - seg_lo) >> 2) : 0u;
+    const f32x4_t *v4 = reinterpret_cast<const f32x4_t *>(row + seg_lo);
+    auto load_batch = [&](f32x4_t (&x)[U], uint32_t base) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t j = base + u * RAG_THREADS + tid;
+            // NaN past the segment: it passes no comparison
+            const float nan = __builtin_nanf("");
+            x[u] = j < n4 ? __builtin_nontemporal_load(v4 + j) : f32x4_t{nan, nan, nan, nan};
+        }
+    };
+    f32x4_t xa[U], xb[U];
+    if (n4) load_batch(xa, 0);
+
     // ---- Phase 1: block-strided view -> coarse histogram -> endpoints.
     for (int i = tid; i < NBINS; i += RAG_THREADS) hist[i] = 0u;
     __syncthreads();
@@ -118,53 +137,56 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
     // ---- Phase 2: certify + collect over [seg_lo, seg_hi).
     Cand *slice = a.slices + cell * (size_t)a.subcap;
     const uint32_t subcap = (uint32_t)a.subcap;
-    uint32_t cnt = 0, c1 = 0;  // wave-uniform
-    auto classify = [&](bool valid, uint32_t i, float x) {
-        const bool in1 = valid && x >= e1;
-        const bool in0 = valid && x >= e0;
-        c1 += (uint32_t)__popcll(__ballot(in1));
-        const uint64_t m0 = __ballot(in0);
-        const uint32_t slot = cnt + lanes_below(m0);
-        if (in0 && slot < subcap) slice[slot] = Cand{i, x};
-        cnt += (uint32_t)__popcll(m0);
+    uint32_t cnt = 0;   // wave-uniform: admitted so far
+    uint32_t c1v = 0;   // per lane: values >= e1
+    // One score: C(tau1) is counted per lane; an admitted score takes the next
+    // slot of the wave's slice (ballot + lane rank).  Past the slice capacity
+    // the last slot is overwritten: the count keeps growing, and a count above
+    // the capacity sends the row to the exact route, which ignores the slice.
+    // Positions past the segment hold NaN, which no comparison admits.
+    auto classify = [&](uint32_t i, float x) {
+        c1v += x >= e1 ? 1u : 0u;
+        const uint64_t m0 = __builtin_amdgcn_fcmpf(x, e0, 3);  // ordered >=, as a lane mask
+        if (x >= e0) {
+            const uint32_t slot =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, cnt));
+            slice[min(slot, subcap - 1u)] = Cand{i, x};
+        }
+        cnt += (uint32_t)__builtin_popcountll(m0);
     };
     if (seg_hi > seg_lo) {
         if (VEC) {
-            constexpr int U = 16;  // all of a thread's 16-byte loads in flight at once
-            const uint32_t n4 = (uint32_t)((seg_hi - seg_lo) >> 2);
-            const f32x4_t *v4 = reinterpret_cast<const f32x4_t *>(row + seg_lo);
-            for (uint32_t base = 0; base < n4; base += RAG_THREADS * U) {
-                f32x4_t x[U];
+            auto classify_batch = [&](const f32x4_t (&x)[U], uint32_t base) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const uint32_t j = base + u * RAG_THREADS + tid;
-                    x[u] = j < n4 ? __builtin_nontemporal_load(v4 + j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    const uint32_t i0 = (uint32_t)seg_lo + 4u * (base + u * RAG_THREADS + tid);
+                    classify(i0 + 0u, x[u].x);
+                    classify(i0 + 1u, x[u].y);
+                    classify(i0 + 2u, x[u].z);
+                    classify(i0 + 3u, x[u].w);
                 }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t j = base + u * RAG_THREADS + tid;
-                    const bool valid = j < n4;
-                    const uint32_t i0 = (uint32_t)seg_lo + 4u * j;
-                    classify(valid, i0 + 0u, x[u].x);
-                    classify(valid, i0 + 1u, x[u].y);
-                    classify(valid, i0 + 2u, x[u].z);
-                    classify(valid, i0 + 3u, x[u].w);
+            };
+            for (uint32_t base = 0; base < n4; base += 2 * BATCH) {
+                if (base + BATCH < n4) load_batch(xb, base + BATCH);
+                classify_batch(xa, base);
+                if (base + BATCH < n4) {
+                    if (base + 2 * BATCH < n4) load_batch(xa, base + 2 * BATCH);
+                    classify_batch(xb, base + BATCH);
                 }
             }
             const uint32_t rem_lo = (uint32_t)seg_lo + 4u * n4;
             if (wave == 0 && rem_lo < (uint32_t)seg_hi) {
                 const uint32_t i = rem_lo + lane;
-                const bool valid = i < (uint32_t)seg_hi;
-                classify(valid, i, valid ? row[i] : 0.f);
+                classify(i, i < (uint32_t)seg_hi ? row[i] : __builtin_nanf(""));
             }
         } else {
             for (int64_t base = seg_lo; base < seg_hi; base += RAG_THREADS) {
                 const int64_t i = base + tid;
-                const bool valid = i < seg_hi;
-                classify(valid, (uint32_t)i, valid ? row[i] : 0.f);
+                classify((uint32_t)i, i < seg_hi ? row[i] : __builtin_nanf(""));
             }
         }
     }
+    const uint32_t c1 = lane_value(wave_incl_sum(c1v), 63);
     if (lane == 0) {
         a.cnt[cell] = cnt;
         a.c1[cell] = c1;
@@ -247,6 +269,8 @@ __device__ uint32_t gather_candidates(const SliceSrc &src, SelectSmem &sm, uint3
     __syncthreads();
     const uint32_t nslice = cpre[src.ncells], total = nslice + src.band_n;
     constexpr int B = 8;  // loads in flight per lane
+    // value range of the gathered items, per wave (select_stashed reads it)
+    float mn = __builtin_inff(), mx = -__builtin_inff();
     for (int c = wave; c < src.ncells; c += blockDim.x >> 6) {
         const uint32_t lo = cpre[c], n = cpre[c + 1] - lo;
         const Cand *cell = src.slices + (size_t)c * src.subcap;
@@ -260,7 +284,11 @@ __device__ uint32_t gather_candidates(const SliceSrc &src, SelectSmem &sm, uint3
 #pragma unroll
             for (int j = 0; j < B; ++j) {
                 const uint32_t i = i0 + j * 64 + lane;
-                if (i < n) sm.stash[lo + i] = make_key(e[j].val, e[j].idx);
+                if (i < n) {
+                    sm.stash[lo + i] = make_key(e[j].val, e[j].idx);
+                    mn = fminf(mn, e[j].val);
+                    mx = fmaxf(mx, e[j].val);
+                }
             }
         }
     }
@@ -274,8 +302,18 @@ __device__ uint32_t gather_candidates(const SliceSrc &src, SelectSmem &sm, uint3
 #pragma unroll
         for (int j = 0; j < B; ++j) {
             const uint32_t i = i0 + j * blockDim.x + tid;
-            if (i < src.band_n) sm.stash[nslice + i] = make_key(e[j].val, e[j].idx);
+            if (i < src.band_n) {
+                sm.stash[nslice + i] = make_key(e[j].val, e[j].idx);
+                mn = fminf(mn, e[j].val);
+                mx = fmaxf(mx, e[j].val);
+            }
         }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+        sm.vmin[wave] = mn;
+        sm.vmax[wave] = mx;
     }
     __syncthreads();
     return total;
@@ -353,7 +391,7 @@ __global__ __launch_bounds__(FIN_THREADS) void k_ragged_finish(RaggedArgs a, int
         const uint32_t bound = route == ROUTE_BAND ? s_c1 : s_c0;
         if (bound <= (uint32_t)STASH_CAP && ncells <= RAG_MAX_CELLS) {
             const uint32_t n = gather_candidates(src, sm, cpre);
-            select_stashed<FIN_THREADS>(sm, n, need, emit);
+            select_stashed<FIN_THREADS>(sm, n, need, emit, true);
         } else {
             exact_select<FIN_THREADS>(sm, src, need, emit);
         }
@@ -368,7 +406,11 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     const Knobs &kn = knobs();
     RaggedPlan p;
     p.M = M; p.pitch = pitch; p.k = k;
+    // about 512 workgroups, and segments of at most 32768 scores (128 KB), so
+    // that long rows do not serialize on one workgroup
     int target = ceil_div_i(512, M);
+    const int by_len = ceil_div_i(pitch > 0 ? pitch : 1, RAG_SEG_MAX);
+    if (target < by_len) target = by_len;
     if (target < 1) target = 1;
     if (target > 16) target = 16;
     if (kn.splits > 0) target = kn.splits;
