@@ -44,8 +44,12 @@ constexpr int RAG_WAVES = RAG_THREADS / 64;
 #ifndef RAG_SEG_MAX
 #define RAG_SEG_MAX 32768
 #endif
-constexpr int RAG_MAX_CELLS = 64;
-constexpr int FIN_THREADS = 1024;  // ragged finisher: one workgroup per row  // (segment, wave) cells per row whose candidates the finisher gathers on chip
+constexpr int RAG_MAX_CELLS = 64;  // (segment, wave) cells per row that the finisher gathers on chip
+// Ragged finisher: one workgroup per row, 1024 threads for up to 255 rows
+// (latency-bound), 512 from 256 rows on (several rows per CU).
+constexpr int FIN_THREADS = 1024;
+constexpr int FIN_THREADS_MANY = 512;
+constexpr int FIN_MANY_ROWS = 256;
 
 struct RaggedPlan {
     int32_t M = 0;
@@ -69,7 +73,10 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
 constexpr int FUSED_WAVES = 8;                  // queries per workgroup
 constexpr int FUSED_THREADS = FUSED_WAVES * 64;
 constexpr int TILE_KEYS = 64;
-constexpr int SEL_THREADS = 512;   // fused select: one workgroup per row
+#ifndef FUSED_SEL_THREADS
+#define FUSED_SEL_THREADS 1024
+#endif
+constexpr int SEL_THREADS = FUSED_SEL_THREADS;  // fused select: one workgroup per row
 constexpr int QROW_MAX_SPLITS = 256;  // single-head path: key splits per query
 
 struct FusedPlan {

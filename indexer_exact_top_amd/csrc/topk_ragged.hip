@@ -9,11 +9,13 @@
 //                   11-bit coarse key in LDS, locates the primary and
 //                   secondary boundaries tau0/tau1 and turns them into
 //                   inclusive fp32 endpoints (Sec. 5.2).  Phase 2: one pass
-//                   over the segment with 16-byte non-temporal loads compares
-//                   each value with the endpoints (Sec. 5.3); admitted values
-//                   are appended to a per-wave slice whose slots come from a
-//                   ballot + popcount + lane-rank (no atomics), and the
-//                   secondary count is accumulated from a second ballot.
+//                   over the segment with 16-byte non-temporal loads (the
+//                   first batch issued before phase 1, later ones double-
+//                   buffered) compares each value with the endpoints
+//                   (Sec. 5.3); admitted values are appended to a per-wave
+//                   slice whose slots come from a compare mask + popcount +
+//                   lane rank (no atomics), and the secondary count is kept
+//                   per lane and summed once per wave.
 //  k_ragged_finish  one workgroup per row.  Sums the per-wave counts and
 //                   picks the route: certified primary, band pass (Sec. 4.3
 //                   "Underfilled views"), or the exact route over the whole
@@ -319,7 +321,8 @@ __device__ uint32_t gather_candidates(const SliceSrc &src, SelectSmem &sm, uint3
     return total;
 }
 
-__global__ __launch_bounds__(FIN_THREADS) void k_ragged_finish(RaggedArgs a, int vec)
+template <int NT>
+__global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
 {
     __shared__ SelectSmem sm;
     __shared__ uint32_t s_c0, s_c1, s_ovf, s_band_n;
@@ -338,14 +341,14 @@ __global__ __launch_bounds__(FIN_THREADS) void k_ragged_finish(RaggedArgs a, int
     const uint32_t my_c1 = has_cell ? a.c1[cell0 + tid] : 0u;
     const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
     int32_t *out = a.out_idx + (size_t)r * a.k;
-    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += FIN_THREADS) out[i] = -1;
+    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += NT) out[i] = -1;
     if (need == 0) {
         if (tid == 0 && a.route) a.route[r] = ROUTE_ALL;
         return;
     }
     if (tid == 0) { s_c0 = 0; s_c1 = 0; s_ovf = 0; s_band_n = 0; }
     __syncthreads();
-    for (int c = tid; c < ncells; c += FIN_THREADS) {
+    for (int c = tid; c < ncells; c += NT) {
         const uint32_t n = c == tid ? my_cnt : a.cnt[cell0 + c];
         atomicAdd(&s_c0, n);
         atomicAdd(&s_c1, c == tid ? my_c1 : a.c1[cell0 + c]);
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(FIN_THREADS) void k_ragged_finish(RaggedArgs a, int
     };
     if (route == ROUTE_EXACT) {
         RowSrc src{row, L, vec != 0};
-        exact_select<FIN_THREADS>(sm, src, need, emit);
+        exact_select<NT>(sm, src, need, emit);
     } else {
         SliceSrc src{a.slices + cell0 * (size_t)a.subcap, a.cnt + cell0, ncells, (uint32_t)a.subcap,
                      a.band + (size_t)r * a.bandcap, route == ROUTE_BAND ? min(s_band_n, (uint32_t)a.bandcap) : 0u};
@@ -391,9 +394,9 @@ __global__ __launch_bounds__(FIN_THREADS) void k_ragged_finish(RaggedArgs a, int
         const uint32_t bound = route == ROUTE_BAND ? s_c1 : s_c0;
         if (bound <= (uint32_t)STASH_CAP && ncells <= RAG_MAX_CELLS) {
             const uint32_t n = gather_candidates(src, sm, cpre);
-            select_stashed<FIN_THREADS>(sm, n, need, emit, true);
+            select_stashed<NT>(sm, n, need, emit, true);
         } else {
-            exact_select<FIN_THREADS>(sm, src, need, emit);
+            exact_select<NT>(sm, src, need, emit);
         }
     }
     if (tid == 0 && a.route) a.route[r] = route;
@@ -473,7 +476,11 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
     if (e != hipSuccess) return e;
     {
         StageTimer st(ST_RAG_FINISH, stream);
-        hipLaunchKernelGGL(k_ragged_finish, dim3(p.M), dim3(FIN_THREADS), 0, stream, a, vec ? 1 : 0);
+        if (p.M >= FIN_MANY_ROWS)
+            hipLaunchKernelGGL(k_ragged_finish<FIN_THREADS_MANY>, dim3(p.M), dim3(FIN_THREADS_MANY), 0, stream, a,
+                               vec ? 1 : 0);
+        else
+            hipLaunchKernelGGL(k_ragged_finish<FIN_THREADS>, dim3(p.M), dim3(FIN_THREADS), 0, stream, a, vec ? 1 : 0);
     }
     return hipGetLastError();
 }
