@@ -154,7 +154,7 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     // count that is a multiple of 8 places each split on one XCD.
     int P = p.G >= 256 ? 1 : (int)ceil_div_u(256, (uint64_t)p.G);
     if (P >= 8) P = (int)ceil_div_u((uint64_t)P, 8) * 8;
-    const int Pmax = (int)(N / 4096) > 1 ? (int)(N / 4096) : 1;
+    const int Pmax = (int)(N / 512) > 1 ? (int)(N / 512) : 1;  // splits of >= 512 keys
     if (P > Pmax) P = Pmax;
     if (kn.splits > 0) P = kn.splits;
     int64_t span = (int64_t)ceil_div_u((uint64_t)N, (uint64_t)P);
