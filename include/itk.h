@@ -123,6 +123,10 @@ itk_status indexer_topk_fused(const void *Q, itk_dtype q_t, const void *K, itk_d
 /* Human-readable name of a status code (static storage). */
 const char *itk_status_string(itk_status status);
 
+/* Name of the HIP runtime error behind the calling thread's most recent
+ * ITK_ERR_HIP ("hipSuccess" if there was none; static storage). */
+const char *itk_last_hip_error(void);
+
 /* ------------------------------------------------------------------------
  * Test and measurement knobs (not needed for normal use).
  * ------------------------------------------------------------------------ */

@@ -41,6 +41,10 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: run indexer_exact_top_amd/build.py (hipcc, gfx950)")
+        # torch first: the library then binds to the HIP runtime that torch
+        # loaded (both name libamdhip64.so.7), so that device pointers and
+        # streams from torch are valid in it
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64, U32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
         L.topk_ragged_workspace_size.argtypes = [I32, I64, I32]
@@ -54,6 +58,8 @@ def lib():
         L.indexer_topk_fused.restype = ctypes.c_int
         L.itk_status_string.argtypes = [ctypes.c_int]
         L.itk_status_string.restype = ctypes.c_char_p
+        L.itk_last_hip_error.argtypes = []
+        L.itk_last_hip_error.restype = ctypes.c_char_p
         L.itk_set_plan_opts.argtypes = [ctypes.POINTER(PlanOpts)]
         L.itk_set_plan_opts.restype = ctypes.c_int
         L.itk_set_route_buffer.argtypes = [P, I32]
@@ -92,6 +98,8 @@ def _stream(stream) -> ctypes.c_void_p:
 
 def _check(status: int, what: str):
     if status != 0:
+        if status == 4:  # ITK_ERR_HIP: name the runtime error
+            what = f"{what} [{lib().itk_last_hip_error().decode()}]"
         raise ITKError(status, what)
 
 

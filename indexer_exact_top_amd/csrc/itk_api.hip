@@ -190,6 +190,7 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
 hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const float *k_scale, const float *W,
                         const int32_t *kv_len, int32_t *out_idx, float *out_score, void *ws, hipStream_t stream)
 {
+    (void)hipGetLastError();  // report only this call's launch errors
     char *w = static_cast<char *>(ws);
     FusedArgs a;
     a.Q = Q; a.K = K; a.k_scale = k_scale; a.W = W; a.kv_len = kv_len;
@@ -227,6 +228,18 @@ using namespace itk;
 
 extern "C" {
 
+// Name of the HIP error behind the last ITK_ERR_HIP of this thread.
+static thread_local hipError_t g_last_hip = hipSuccess;
+
+static itk_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return ITK_OK;
+    g_last_hip = e;
+    return ITK_ERR_HIP;
+}
+
+const char *itk_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
+
 const char *itk_status_string(itk_status s)
 {
     switch (s) {
@@ -255,7 +268,7 @@ itk_status topk_ragged(const float *scores, int64_t row_pitch, const int32_t *ro
     if (!workspace || workspace_bytes < p.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return ITK_ERR_WORKSPACE;
     const hipError_t e = launch_ragged(p, scores, row_len, out_idx, workspace, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+    return hip_status(e);
 }
 
 size_t indexer_topk_fused_workspace_size(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk_dtype q_t,
@@ -281,7 +294,7 @@ itk_status indexer_topk_fused(const void *Q, itk_dtype q_t, const void *K, itk_d
         return ITK_ERR_WORKSPACE;
     const hipError_t e = launch_fused(p, Q, K, k_scale, W, kv_len, out_idx, out_score, workspace,
                                       static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+    return hip_status(e);
 }
 
 itk_status itk_set_plan_opts(const itk_plan_opts *o)

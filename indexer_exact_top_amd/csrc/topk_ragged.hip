@@ -449,6 +449,9 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
 hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t *row_len, int32_t *out_idx,
                          void *ws, hipStream_t stream)
 {
+    // An error left by an earlier, unrelated runtime call would otherwise be
+    // reported as this launch's failure.
+    (void)hipGetLastError();
     char *w = static_cast<char *>(ws);
     RaggedArgs a;
     a.scores = scores;
