@@ -42,6 +42,8 @@ def test_config1_all_rows(itk):
     (synth.BF16, synth.BF16, 64, 128), (synth.BF16, synth.BF16, 8, 64), (synth.BF16, synth.BF16, 33, 64),
     (synth.BF16, synth.FP8_E4M3, 64, 128), (synth.F16, synth.F16, 16, 256), (synth.F16, synth.FP8_E4M3, 32, 128),
     (synth.F32, synth.F32, 8, 128), (synth.F32, synth.F32, 40, 64),
+    # one head: the queries-as-columns kernels (16-bit keys copied to LDS, FP8 keys through registers)
+    (synth.BF16, synth.BF16, 1, 64), (synth.F16, synth.FP8_E4M3, 1, 128), (synth.BF16, synth.FP8_E4M3, 1, 256),
 ])
 def test_dtype_shapes(itk, qt, kt, H, D):
     T, N, k = 19, 9000, 300
@@ -139,3 +141,21 @@ def test_full_size_sampled_rows(itk, cfg, rows, min_recall):
         assert ((sel >= 0) & (sel < case.kv_len[t])).all()
         assert np.unique(sel).size == need[t]
     print(f"config{cfg} full size: recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
+
+
+@pytest.mark.parametrize("relu", [False, True])
+def test_single_head_signed_weights(itk, relu):
+    # Negative, zero and negative-zero weights: without ReLU the sign is folded
+    # into the query operands; with ReLU a negative weight makes every score
+    # non-positive and each accumulator is tested exactly.
+    case = synth.gen_fused(70, 1, 128, 20000, 300, q_dtype=synth.F16, k_dtype=synth.F16, no_relu=not relu,
+                           unit_norm=not relu, seed=77 + relu)
+    rng = np.random.default_rng(5)
+    W = rng.uniform(-1.0, 1.0, size=(case.T, 1)).astype(np.float32)
+    W[0, 0] = 0.0
+    W[1, 0] = -0.0
+    W[2, 0] = -1.0
+    case.W = W
+    idx, sc, routes = _run(itk, case, routes=True)
+    print("routes", np.bincount(routes).tolist())
+    check_fused_rows(case, range(case.T), idx, sc, min_recall=0.95)
