@@ -47,6 +47,17 @@ typedef enum {
  * LiteTopK Sec. 3.1 Eq. (2)); requires H == 1; W[t,0] still multiplies. */
 #define ITK_FLAG_NO_RELU 1u
 
+/* Fused call, FP8 keys only: score with the FP8 matrix cores.  Each
+ * (query, head) row of Q is quantized to e4m3fn with its own scale
+ * max|Q[t,h,:]| / 448 (round to nearest even), the scale is folded into
+ * W[t,h] (exact up to fp32 rounding, since ReLU commutes with a positive
+ * factor), and Q8 . K8 runs on v_mfma_scale_f32_32x32x64_f8f6f4.  The scores
+ * then approximate the definition by the quantization of Q (the DSA indexer
+ * of LiteTopK Sec. 2.1 keeps FP8 keys for this product); the Top-k is exact
+ * on those scores.  Requires k_t == ITK_FP8_E4M3, q_t BF16 or F16, H >= 2
+ * (ITK_ERR_UNSUPPORTED otherwise). */
+#define ITK_FLAG_FP8_SCORE 2u
+
 /* ------------------------------------------------------------------------
  * Standalone exact Top-k over materialized ragged fp32 rows.
  *

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libitk.so")
 
 F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
 FLAG_NO_RELU = 1
+FLAG_FP8_SCORE = 2  # FP8 keys: quantize Q per (query, head) row and score on the FP8 matrix cores
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip error"}
 
 _lib = None

@@ -2,8 +2,9 @@
 #include "fused_qrow.hpp"
 
 namespace itk {
-FusedLauncher find_fused_launcher_bf16(int qt, int kt, int hb, int d, bool relu)
+FusedLauncher find_fused_launcher_bf16(int qt, int kt, int hb, int d, bool relu, bool q8)
 {
+    ITK_FUSED_Q8_CASES_FOR(ITK_BF16)
     ITK_FUSED_CASES_FOR(ITK_BF16, ITK_BF16)
     ITK_FUSED_CASES_FOR(ITK_BF16, ITK_FP8_E4M3)
     return nullptr;

@@ -46,8 +46,10 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-enum MType { M_BF16 = 0, M_F16 = 1, M_F32 = 2 };
+enum MType { M_BF16 = 0, M_F16 = 1, M_F32 = 2, M_FP8 = 3 };
 
 template <int MT>
 struct MTraits;
@@ -66,6 +68,11 @@ struct MTraits<M_F32> {
     using frag = float;
     static constexpr int ebytes = 4, kstep = 2, pad = 16;
 };
+template <>
+struct MTraits<M_FP8> {  // e4m3fn x e4m3fn, 64-element k-steps, 32 bytes per lane
+    using frag = u32x8_t;
+    static constexpr int ebytes = 1, kstep = 64, pad = 16;
+};
 
 template <int MT>
 __device__ __forceinline__ f32x16_t mfma32(typename MTraits<MT>::frag a, typename MTraits<MT>::frag b, f32x16_t c)
@@ -76,6 +83,9 @@ __device__ __forceinline__ f32x16_t mfma32(typename MTraits<MT>::frag a, typenam
     else if constexpr (MT == M_F16)
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else if constexpr (MT == M_FP8)  // both operands e4m3fn (format 0), unit block scales (E8M0 127)
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8_t, a),
+                                                               __builtin_bit_cast(i32x8_t, b), c, 0, 0, 0, 127, 0, 127);
     else
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -108,12 +118,15 @@ __device__ __forceinline__ u32x2_t fp8x4_widen(uint32_t word)
 // Staging: 16- and 32-bit keys are copied global -> LDS by the direct
 // LDS-load path (no registers, no LDS write instructions), in stages of
 // STAGE_KEYS keys; FP8 keys go through registers to be widened once per
-// workgroup, in stages of 64 keys.
-template <int QT_, int KT_, int HB_, int D_, bool RELU_>
+// workgroup, in stages of 64 keys, unless the queries are quantized to FP8
+// too (Q8): then the raw key bytes are copied like 16-bit keys and the
+// contraction runs on the FP8 matrix cores.
+template <int QT_, int KT_, int HB_, int D_, bool RELU_, bool Q8_ = false>
 struct FCfg {
     static constexpr int QT = QT_, KT = KT_, HB = HB_, D = D_;
-    static constexpr bool RELU = RELU_;
-    static constexpr int MT = (QT == ITK_F32) ? M_F32 : (QT == ITK_BF16 ? M_BF16 : M_F16);
+    static constexpr bool RELU = RELU_, Q8 = Q8_;
+    static_assert(!Q8 || KT == ITK_FP8_E4M3, "FP8 scoring needs FP8 keys");
+    static constexpr int MT = Q8 ? M_FP8 : (QT == ITK_F32) ? M_F32 : (QT == ITK_BF16 ? M_BF16 : M_F16);
     using TR = MTraits<MT>;
     using frag = typename TR::frag;
     static constexpr int KS = D / TR::kstep;                 // MFMA k-steps
@@ -124,7 +137,7 @@ struct FCfg {
     static constexpr int kbytes = (KT == ITK_F32) ? 4 : (KT == ITK_FP8_E4M3 ? 1 : 2);
     static constexpr int qbytes = (QT == ITK_F32) ? 4 : 2;
     static constexpr bool SCALE = (KT == ITK_FP8_E4M3);
-    static constexpr bool DMA = !SCALE;
+    static constexpr bool DMA = !SCALE || Q8;
     static constexpr int STAGE_KEYS = DMA ? (ROWB <= 256 ? 128 : 64) : TILE_KEYS;
     static constexpr int NSUB = STAGE_KEYS / TILE_KEYS;      // 64-key tiles per stage
     static constexpr int TILE_LDS = TILE_KEYS * ROWP;        // LDS bytes of one 64-key tile
@@ -206,6 +219,14 @@ struct QFrags {
 
     __device__ void load(const FusedArgs &a, int t)
     {
+        if constexpr (C::MT == M_FP8)
+            load_q8(a, t);
+        else
+            load_16_32(a, t);
+    }
+
+    __device__ void load_16_32(const FusedArgs &a, int t)
+    {
         const int l = (int)lane_id();
         const int H = a.H;
 #pragma unroll
@@ -226,6 +247,76 @@ struct QFrags {
             for (int r = 0; r < 16; ++r) {
                 const int h = hb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
                 w[hb][r] = h < H ? a.W[(size_t)t * H + h] : 0.f;
+            }
+        }
+    }
+
+    // FP8 scoring: each (query, head) row is quantized to e4m3fn with its own
+    // scale amax / 448 (round to nearest even; |q| / scale <= 448 is finite),
+    // and the scale is folded into the head weight, which is exact to fp32
+    // rounding because ReLU commutes with a positive factor:
+    //   w * ReLU(q . k) ~= (w * scale) * ReLU((q / scale) . k).
+    // Lane l holds head l % 32 and the 32 elements 64 kk + 32 (l / 32) of each
+    // k-step; the B fragments of the keys use the same element order.
+    __device__ void load_q8(const FusedArgs &a, int t)
+    {
+        const int l = (int)lane_id();
+        const int H = a.H;
+        const int half = l >> 5;
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb) {
+            const int head = hb * 32 + (l & 31);
+            const bool ok = head < H;
+            float x[C::KS][32];
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk) {
+                const int d0 = kk * 64 + 32 * half;
+                const char *ptr = static_cast<const char *>(a.Q) + (((size_t)t * H + (ok ? head : 0)) * C::D + d0) * 2;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t *>(ptr + 16 * c) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t wd = v[e];
+                        if constexpr (C::QT == ITK_BF16) {
+                            x[kk][8 * c + 2 * e] = __uint_as_float(wd << 16);
+                            x[kk][8 * c + 2 * e + 1] = __uint_as_float(wd & 0xFFFF0000u);
+                        } else {
+                            x[kk][8 * c + 2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xFFFFu));
+                            x[kk][8 * c + 2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+                        }
+                    }
+                }
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+                for (int i = 0; i < 32; ++i) amax = fmaxf(amax, __builtin_fabsf(x[kk][i]));
+            // lanes l and l ^ 32 hold the two halves of the same row
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+            amax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            const bool pos = amax > 0.f && __builtin_isfinite(amax);
+            const float inv = pos ? 448.f / amax : 0.f;
+            const float qs = pos ? amax / 448.f : 1.f;
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk) {
+                u32x8_t f;
+#pragma unroll
+                for (int wd = 0; wd < 8; ++wd) {
+                    int v = 0;
+                    v = __builtin_amdgcn_cvt_pk_fp8_f32(x[kk][4 * wd] * inv, x[kk][4 * wd + 1] * inv, v, false);
+                    v = __builtin_amdgcn_cvt_pk_fp8_f32(x[kk][4 * wd + 2] * inv, x[kk][4 * wd + 3] * inv, v, true);
+                    f[wd] = (uint32_t)v;
+                }
+                q[hb][kk] = f;
+            }
+            // weights of the accumulator rows this lane holds, times their rows' scales
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int h = hb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const float sc = __shfl(qs, h & 31);
+                w[hb][r] = h < H ? a.W[(size_t)t * H + h] * sc : 0.f;
             }
         }
     }
@@ -301,6 +392,8 @@ __device__ __forceinline__ void block_mfma(f32x16_t (&acc)[C::HB], const QFrags<
             const int kk = k0 + i;
             if constexpr (C::MT == M_F32)
                 b[i] = *reinterpret_cast<const float *>(bl + kk * 8);
+            else if constexpr (C::MT == M_FP8)
+                b[i] = *reinterpret_cast<const u32x8_t *>(bl + kk * 64);
             else
                 b[i] = *reinterpret_cast<const u32x4_t *>(bl + kk * 32);
         }
@@ -316,7 +409,7 @@ template <class C>
 __device__ __forceinline__ int bfrag_lane_off()
 {
     const int l = (int)lane_id();
-    return (l & 31) * C::ROWP + (C::MT == M_F32 ? (l >> 5) * 4 : (l >> 5) * 16);
+    return (l & 31) * C::ROWP + (C::MT == M_F32 ? (l >> 5) * 4 : C::MT == M_FP8 ? (l >> 5) * 32 : (l >> 5) * 16);
 }
 
 // Scheduling hint for one block: per chunk, the B-fragment LDS reads, then
@@ -360,6 +453,9 @@ __device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int
             typename C::frag b;
             if constexpr (C::MT == M_F32) {
                 b = ok ? reinterpret_cast<const float *>(krow)[kk * 2 + (l >> 5)] : 0.f;
+            } else if constexpr (C::MT == M_FP8) {
+                const int d0 = kk * 64 + 32 * (l >> 5);
+                b = ok ? *reinterpret_cast<const u32x8_t *>(krow + d0) : u32x8_t{};
             } else if constexpr (C::KT == ITK_FP8_E4M3) {
                 const int d0 = kk * 16 + 8 * (l >> 5);
                 const u32x2_t raw = ok ? *reinterpret_cast<const u32x2_t *>(krow + d0) : u32x2_t{0u, 0u};
@@ -382,7 +478,24 @@ __device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int
 template <class C>
 struct TileBuf {
     char k[2][C::STAGE_BYTES];
-    float scale[2][TILE_KEYS];
+    float scale[2][C::SCALE ? C::STAGE_KEYS : 1];
+};
+
+// Per-key FP8 scales of a stage whose key bytes are copied straight to LDS:
+// thread i < NSUB * 64 loads the scale of key i of the stage into a register
+// when the stage's copy is issued, and stores it to LDS after the copy's wait.
+template <class C, int NSUB>
+struct ScaleStage {
+    float v = 1.f;
+    __device__ __forceinline__ void load(const FusedArgs &a, int64_t key0)
+    {
+        const int64_t key = key0 + (int64_t)threadIdx.x;
+        if (threadIdx.x < NSUB * TILE_KEYS) v = key < a.N ? a.k_scale[key] : 0.f;
+    }
+    __device__ __forceinline__ void store(TileBuf<C> &tb, int buf) const
+    {
+        if (threadIdx.x < NSUB * TILE_KEYS) tb.scale[buf][threadIdx.x] = v;
+    }
 };
 
 // One wave instruction of the direct global -> LDS copy: lane i's 16 bytes
@@ -534,10 +647,13 @@ __device__ __forceinline__ void scan_tiles(const FusedArgs &a, TileBuf<C> &tb, c
     const int64_t kend = key_end < (int64_t)L ? key_end : (int64_t)L;
     KStage<C> ks;
     DmaPlan<C, NSUB> dp;
+    ScaleStage<C, NSUB> ss;
+    constexpr bool DSCALE = C::DMA && C::SCALE;  // scales beside copied FP8 key bytes
     if constexpr (C::DMA) dp.init();
     if (nstages > 0) {
         if constexpr (C::DMA) {
             dp.issue(a, tb, 0, first);
+            if constexpr (DSCALE) ss.load(a, first);
         } else {
             ks.load(a, first);
             ks.store(tb, 0);
@@ -545,6 +661,7 @@ __device__ __forceinline__ void scan_tiles(const FusedArgs &a, TileBuf<C> &tb, c
     }
     const_cast<QFrags<C> &>(qf).settle();
     wait_vmem_all();
+    if constexpr (DSCALE) ss.store(tb, 0);
     __syncthreads();
     f32x16_t accA[C::HB], accB[C::HB];
 #pragma unroll
@@ -559,8 +676,12 @@ __device__ __forceinline__ void scan_tiles(const FusedArgs &a, TileBuf<C> &tb, c
         const int64_t skey = first + (int64_t)st * step;
         const int buf = st & 1;
         if (st + 1 < nstages) {
-            if constexpr (C::DMA) dp.issue(a, tb, buf ^ 1, skey + step);
-            else ks.load(a, skey + step);
+            if constexpr (C::DMA) {
+                dp.issue(a, tb, buf ^ 1, skey + step);
+                if constexpr (DSCALE) ss.load(a, skey + step);
+            } else {
+                ks.load(a, skey + step);
+            }
         }
 #pragma unroll
         for (int sub = 0; sub < NSUB; ++sub) {
@@ -579,7 +700,7 @@ __device__ __forceinline__ void scan_tiles(const FusedArgs &a, TileBuf<C> &tb, c
                 p0 = reduce_block<C>(accA, qf.w);
                 sched_block<C>();
                 asm volatile("" : "+v"(p0));
-                if constexpr (C::SCALE) psc = tb.scale[buf][lane];
+                if constexpr (C::SCALE) psc = tb.scale[buf][sub * TILE_KEYS + lane];
                 pend = key0;
             } else if (pend >= 0) {
                 const float p1 = reduce_block<C>(accB, qf.w);
@@ -590,6 +711,7 @@ __device__ __forceinline__ void scan_tiles(const FusedArgs &a, TileBuf<C> &tb, c
         if (st + 1 < nstages) {
             if constexpr (!C::DMA) ks.store(tb, buf ^ 1);
             wait_vmem_all();
+            if constexpr (DSCALE) ss.store(tb, buf ^ 1);
         }
         __syncthreads();
     }
@@ -907,7 +1029,7 @@ struct RescoreSrc {
 enum { FROUTE_SAMPLE = 1, FROUTE_RECOVER = 3, FROUTE_ALL = 4 };
 
 template <class C>
-__global__ __launch_bounds__(SEL_THREADS) void k_fused_select(FusedArgs a)
+__global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
 {
     __shared__ SelectSmem sm;
     const int tid = threadIdx.x;
@@ -916,7 +1038,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_fused_select(FusedArgs a)
     const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
     int32_t *oi = a.out_idx + (size_t)t * a.k;
     float *os = a.out_score + (size_t)t * a.k;
-    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += SEL_THREADS) {
+    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += SEL_THREADS_HR) {
         oi[i] = -1;
         os[i] = -__builtin_inff();
     }
@@ -938,27 +1060,27 @@ __global__ __launch_bounds__(SEL_THREADS) void k_fused_select(FusedArgs a)
             // all candidates fit on chip: one parallel copy, then every
             // refinement round reads LDS only
             constexpr int B = 8;  // loads in flight per thread
-            for (uint32_t i0 = 0; i0 < n; i0 += SEL_THREADS * B) {
+            for (uint32_t i0 = 0; i0 < n; i0 += SEL_THREADS_HR * B) {
                 Cand e[B];
 #pragma unroll
                 for (int j = 0; j < B; ++j) {
-                    const uint32_t i = i0 + j * SEL_THREADS + tid;
+                    const uint32_t i = i0 + j * SEL_THREADS_HR + tid;
                     if (i < n) e[j] = src.c[i];
                 }
 #pragma unroll
                 for (int j = 0; j < B; ++j) {
-                    const uint32_t i = i0 + j * SEL_THREADS + tid;
+                    const uint32_t i = i0 + j * SEL_THREADS_HR + tid;
                     if (i < n) sm.stash[i] = make_key(e[j].val, e[j].idx);
                 }
             }
             __syncthreads();
-            select_stashed<SEL_THREADS>(sm, n, need, emit);
+            select_stashed<SEL_THREADS_HR>(sm, n, need, emit);
         } else {
-            exact_select<SEL_THREADS>(sm, src, need, emit);
+            exact_select<SEL_THREADS_HR>(sm, src, need, emit);
         }
     } else {
         RescoreSrc<C> src{&a, t, L};
-        exact_select<SEL_THREADS>(sm, src, need, emit);
+        exact_select<SEL_THREADS_HR>(sm, src, need, emit);
     }
     if (tid == 0 && a.route) {
         const float4 bp = a.param[t];
@@ -989,7 +1111,7 @@ hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         StageTimer st(ST_F_SELECT, stream);
-        hipLaunchKernelGGL(k_fused_select<C>, dim3(p.T), dim3(SEL_THREADS), 0, stream, a);
+        hipLaunchKernelGGL(k_fused_select<C>, dim3(p.T), dim3(SEL_THREADS_HR), 0, stream, a);
     }
     return hipGetLastError();
 }
@@ -997,7 +1119,7 @@ hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t 
 using FusedLauncher = hipError_t (*)(const FusedPlan &, const FusedArgs &, hipStream_t);
 
 // Registry of instantiated configurations (filled by the per-dtype units).
-FusedLauncher find_fused_launcher(int qt, int kt, int hb, int d, bool relu);
+FusedLauncher find_fused_launcher(int qt, int kt, int hb, int d, bool relu, bool q8);
 
 #define ITK_FUSED_CASES_FOR(QT, KT)                                                               \
     if (qt == QT && kt == KT) {                                                                   \
@@ -1012,6 +1134,19 @@ FusedLauncher find_fused_launcher(int qt, int kt, int hb, int d, bool relu);
             if (hb == 1 && d == 128) return &launch_fused_cfg<FCfg<QT, KT, 1, 128, false>>;       \
             if (hb == 1 && d == 256) return &launch_fused_cfg<FCfg<QT, KT, 1, 256, false>>;       \
         }                                                                                         \
+    }
+
+// FP8 scoring (queries quantized per row, FP8 keys copied raw).
+#define ITK_FUSED_Q8_CASES_FOR(QT)                                                                \
+    if (qt == QT && kt == ITK_FP8_E4M3 && q8) {                                                   \
+        if (relu) {                                                                               \
+            if (hb == 1 && d == 64) return &launch_fused_cfg<FCfg<QT, ITK_FP8_E4M3, 1, 64, true, true>>;   \
+            if (hb == 1 && d == 128) return &launch_fused_cfg<FCfg<QT, ITK_FP8_E4M3, 1, 128, true, true>>; \
+            if (hb == 1 && d == 256) return &launch_fused_cfg<FCfg<QT, ITK_FP8_E4M3, 1, 256, true, true>>; \
+            if (hb == 2 && d == 64) return &launch_fused_cfg<FCfg<QT, ITK_FP8_E4M3, 2, 64, true, true>>;   \
+            if (hb == 2 && d == 128) return &launch_fused_cfg<FCfg<QT, ITK_FP8_E4M3, 2, 128, true, true>>; \
+        }                                                                                         \
+        return nullptr;                                                                           \
     }
 
 // fp32 operands: ceil(H/32) * D <= 128 keeps the Q fragments within budget.

@@ -21,9 +21,9 @@ RouteSink &route_sink()
     return r;
 }
 
-FusedLauncher find_fused_launcher_bf16(int, int, int, int, bool);
-FusedLauncher find_fused_launcher_f16(int, int, int, int, bool);
-FusedLauncher find_fused_launcher_f32(int, int, int, int, bool);
+FusedLauncher find_fused_launcher_bf16(int, int, int, int, bool, bool);
+FusedLauncher find_fused_launcher_f16(int, int, int, int, bool, bool);
+FusedLauncher find_fused_launcher_f32(int, int, int, int, bool, bool);
 
 FusedLauncher find_qrow_launcher_bf16(int, int, int, bool);
 FusedLauncher find_qrow_launcher_f16(int, int, int, bool);
@@ -35,11 +35,11 @@ FusedLauncher find_qrow_launcher(int qt, int kt, int d, bool relu)
     return nullptr;
 }
 
-FusedLauncher find_fused_launcher(int qt, int kt, int hb, int d, bool relu)
+FusedLauncher find_fused_launcher(int qt, int kt, int hb, int d, bool relu, bool q8)
 {
-    if (qt == ITK_BF16) return find_fused_launcher_bf16(qt, kt, hb, d, relu);
-    if (qt == ITK_F16) return find_fused_launcher_f16(qt, kt, hb, d, relu);
-    if (qt == ITK_F32) return find_fused_launcher_f32(qt, kt, hb, d, relu);
+    if (qt == ITK_BF16) return find_fused_launcher_bf16(qt, kt, hb, d, relu, q8);
+    if (qt == ITK_F16) return find_fused_launcher_f16(qt, kt, hb, d, relu, q8);
+    if (qt == ITK_F32) return find_fused_launcher_f32(qt, kt, hb, d, relu, q8);
     return nullptr;
 }
 
@@ -86,8 +86,10 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     if (T <= 0 || H <= 0 || D <= 0 || N <= 0 || k <= 0) return ITK_ERR_INVALID_ARG;
     if (N > (int64_t)0x7FFFFFFF) return ITK_ERR_UNSUPPORTED;
     if (qt < ITK_F32 || qt > ITK_FP8_E4M3 || kt < ITK_F32 || kt > ITK_FP8_E4M3) return ITK_ERR_INVALID_ARG;
-    if (flags & ~ITK_FLAG_NO_RELU) return ITK_ERR_INVALID_ARG;
+    if (flags & ~(ITK_FLAG_NO_RELU | ITK_FLAG_FP8_SCORE)) return ITK_ERR_INVALID_ARG;
     if ((flags & ITK_FLAG_NO_RELU) && H != 1) return ITK_ERR_INVALID_ARG;
+    const bool q8 = (flags & ITK_FLAG_FP8_SCORE) != 0;
+    if (q8 && (kt != ITK_FP8_E4M3 || qt == ITK_F32 || H < 2)) return ITK_ERR_UNSUPPORTED;
     if (H > 64) return ITK_ERR_UNSUPPORTED;
     if (D != 64 && D != 128 && D != 256) return ITK_ERR_UNSUPPORTED;
     const bool pair_ok = (qt == ITK_BF16 && (kt == ITK_BF16 || kt == ITK_FP8_E4M3)) ||
@@ -98,7 +100,7 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     if (HB == 2 && D > 128) return ITK_ERR_UNSUPPORTED;
     if (qt == ITK_F32 && HB * D > 128) return ITK_ERR_UNSUPPORTED;
     const bool relu = !(flags & ITK_FLAG_NO_RELU);
-    if (!find_fused_launcher(qt, kt, HB, D, relu)) return ITK_ERR_UNSUPPORTED;
+    if (!find_fused_launcher(qt, kt, HB, D, relu, q8)) return ITK_ERR_UNSUPPORTED;
 
     const Knobs &kn = knobs();
     FusedPlan p;
@@ -217,7 +219,8 @@ hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const 
         if (!fn) return hipErrorInvalidValue;
         return fn(p, a, stream);
     }
-    FusedLauncher fn = find_fused_launcher(p.qt, p.kt, p.HB, p.D, !(p.flags & ITK_FLAG_NO_RELU));
+    FusedLauncher fn = find_fused_launcher(p.qt, p.kt, p.HB, p.D, !(p.flags & ITK_FLAG_NO_RELU),
+                                           (p.flags & ITK_FLAG_FP8_SCORE) != 0);
     if (!fn) return hipErrorInvalidValue;
     return fn(p, a, stream);
 }

@@ -73,10 +73,12 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
 constexpr int FUSED_WAVES = 8;                  // queries per workgroup
 constexpr int FUSED_THREADS = FUSED_WAVES * 64;
 constexpr int TILE_KEYS = 64;
-#ifndef FUSED_SEL_THREADS
-#define FUSED_SEL_THREADS 1024
-#endif
-constexpr int SEL_THREADS = FUSED_SEL_THREADS;  // fused select: one workgroup per row
+// Fused select, one workgroup per row: the single-head kernels use 1024
+// threads; the head-rows kernel uses 512, because its recovery route holds a
+// query's fragments and weights in registers (a 1024-thread workgroup leaves
+// 128 VGPRs per lane, which makes it spill).
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_THREADS_HR = 512;
 constexpr int QROW_MAX_SPLITS = 256;  // single-head path: key splits per query
 
 struct FusedPlan {

@@ -66,3 +66,53 @@ def check_ragged_exact(case, gpu_idx, rows=None):
             miss = np.setdiff1d(exp, got)[:8]
             extra = np.setdiff1d(got, exp)[:8]
             raise AssertionError(f"row {m} (L={case.row_len[m]}): missing {miss.tolist()} extra {extra.tolist()}")
+
+
+def fp8_score_bound(case, t, idx):
+    """Bound on |score - exact score| when query row (t, h) is quantized to
+    e4m3fn with scale s_h = max|q[t,h,:]| / 448 (round to nearest even):
+    each element moves by at most 2^-4 of itself (3 mantissa bits) or, below
+    the normal range, by 2^-10 s_h; ReLU is 1-Lipschitz, so
+        |ds| <= sum_h |w_h| sum_d (2^-4 |q_hd| + 2^-10 s_h) |k_d|,
+    plus fp32 accumulation (covered by a 10% margin)."""
+    q = oracle.decode(case.q_bits[t], case.q_dtype).reshape(case.H, case.D)
+    k = oracle.decode(case.k_bits[np.asarray(idx)], case.k_dtype).reshape(len(idx), case.D)
+    if case.k_scale is not None:
+        k = k * case.k_scale[np.asarray(idx)].astype(np.float64)[:, None]
+    s = np.abs(q).max(axis=1) / 448.0
+    w = np.abs(case.W[t].astype(np.float64))
+    ak = np.abs(k)
+    per_head = (2.0 ** -4) * (np.abs(q) @ ak.T) + (2.0 ** -10) * s[:, None] * ak.sum(axis=1)[None, :]
+    return 1.1 * (w[:, None] * per_head).sum(axis=0)
+
+
+def check_fp8_score_rows(case, rows, gpu_idx, gpu_score, min_recall=None):
+    """FP8-scoring results: invariants, each returned score within the
+    quantization bound of its exact score, and no returned index whose exact
+    score lies further below the exact k-th score than the two bounds allow."""
+    rows = np.asarray(rows, dtype=np.int32)
+    o_idx, o_val, o_n = oracle.fused_topk(case, rows=rows)
+    recalls = []
+    for r, t in enumerate(rows):
+        L = int(case.kv_len[t])
+        need = min(case.k, max(L, 0))
+        gi, gs = np.asarray(gpu_idx[t]), np.asarray(gpu_score[t])
+        assert o_n[r] == need
+        assert (gi[need:] == -1).all() and np.isneginf(gs[need:]).all(), f"row {t}: padding"
+        sel = gi[:need]
+        assert len(np.unique(sel)) == need and ((sel >= 0) & (sel < L)).all(), f"row {t}: invalid indices"
+        if need == 0:
+            recalls.append(1.0)
+            continue
+        ora_sel = oracle.fused_scores_at(case, np.full(need, t), sel)
+        b_sel = fp8_score_bound(case, t, sel)
+        err = np.abs(gs[:need].astype(np.float64) - ora_sel)
+        assert (err <= b_sel).all(), f"row {t}: score error {(err / b_sel).max():.3g} x the bound"
+        kth = o_val[r, need - 1]
+        b_ora = fp8_score_bound(case, t, o_idx[r, :need])
+        assert (ora_sel >= kth - b_sel - b_ora.max()).all(), f"row {t}: a selected score is too low"
+        recalls.append(len(set(sel.tolist()) & set(o_idx[r, :need].tolist())) / need)
+    recalls = np.asarray(recalls)
+    if min_recall is not None:
+        assert recalls.min() >= min_recall, f"recall {recalls.min():.4f} < {min_recall}"
+    return recalls

@@ -73,6 +73,9 @@ def test_fused_validation():
     assert call(args(qt=F32, kt=F32, H=40, D=128)) == 2
     assert call(args(flags=1, H=2)) == 1            # NO_RELU needs H == 1
     assert call(args(flags=4)) == 1
+    assert call(args(flags=2)) == 2                 # FP8 scoring needs FP8 keys
+    assert call(args(flags=2, kt=FP8, S=FAKE, qt=F32)) == 2
+    assert call(args(flags=3, kt=FP8, S=FAKE, H=1)) == 2  # ... and at least two heads
     assert call(args(Q=P(0x10004))) == 1            # misaligned
     assert call(args(ws=None)) == 3
     assert call(args(wsb=16)) == 3

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import synth
-from parity import check_fused_rows
+from parity import check_fp8_score_rows, check_fused_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -159,3 +159,30 @@ def test_single_head_signed_weights(itk, relu):
     idx, sc, routes = _run(itk, case, routes=True)
     print("routes", np.bincount(routes).tolist())
     check_fused_rows(case, range(case.T), idx, sc, min_recall=0.95)
+
+
+# FP8 scoring (queries quantized per row, e4m3 x e4m3 matrix cores): the scores
+# approximate the definition, so the parity bar is the quantization bound of
+# each score (parity.fp8_score_bound) plus the invariants; recall is reported.  Every route computes the same
+# quantized scores, so forced recovery returns the same sets.
+@pytest.mark.parametrize("qt,H,D", [(synth.BF16, 64, 128), (synth.F16, 32, 64), (synth.BF16, 20, 256),
+                                    (synth.BF16, 40, 64)])
+def test_fp8_scoring(itk, qt, H, D):
+    kv = np.array([30000, 29999, 20000, 513, 512, 511, 1, 0] + [30000 - 911 * i for i in range(8)], dtype=np.int32)
+    case = synth.gen_fused(16, H, D, 30000, 512, q_dtype=qt, k_dtype=synth.FP8_E4M3, kv_len=kv, seed=H + D)
+    case.flags = itk.FLAG_FP8_SCORE
+    idx, sc, routes = _run(itk, case, routes=True)
+    rec = check_fp8_score_rows(case, range(case.T), idx, sc, min_recall=0.8)
+    print(f"fp8 scoring H={H} D={D}: recall mean {rec.mean():.4f} min {rec.min():.4f}; routes",
+          np.bincount(routes).tolist())
+    itk.set_plan_opts(force_route=1)
+    got, _, _ = _run(itk, case)
+    assert np.array_equal(np.sort(idx, axis=1), np.sort(got, axis=1))
+
+
+def test_fp8_scoring_config4_sampled_rows(itk):
+    case = synth.fused_config(4)
+    case.flags = itk.FLAG_FP8_SCORE
+    idx, sc, routes = _run(itk, case, routes=True)
+    rec = check_fp8_score_rows(case, [0, 64, 127], idx, sc, min_recall=0.8)
+    print(f"config4 fp8 scoring: recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
