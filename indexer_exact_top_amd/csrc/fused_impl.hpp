@@ -1060,6 +1060,7 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
             // all candidates fit on chip: one parallel copy, then every
             // refinement round reads LDS only
             constexpr int B = 8;  // loads in flight per thread
+            float mn = __builtin_inff(), mx = -__builtin_inff();  // value range, taken on the way
             for (uint32_t i0 = 0; i0 < n; i0 += SEL_THREADS_HR * B) {
                 Cand e[B];
 #pragma unroll
@@ -1070,11 +1071,21 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
 #pragma unroll
                 for (int j = 0; j < B; ++j) {
                     const uint32_t i = i0 + j * SEL_THREADS_HR + tid;
-                    if (i < n) sm.stash[i] = make_key(e[j].val, e[j].idx);
+                    if (i < n) {
+                        sm.stash[i] = make_key(e[j].val, e[j].idx);
+                        mn = fminf(mn, e[j].val);
+                        mx = fmaxf(mx, e[j].val);
+                    }
                 }
             }
+            mn = wave_min(mn);
+            mx = wave_max(mx);
+            if ((tid & 63) == 0) {
+                sm.vmin[tid >> 6] = mn;
+                sm.vmax[tid >> 6] = mx;
+            }
             __syncthreads();
-            select_stashed<SEL_THREADS_HR>(sm, n, need, emit);
+            select_stashed<SEL_THREADS_HR>(sm, n, need, emit, true);
         } else {
             exact_select<SEL_THREADS_HR>(sm, src, need, emit);
         }

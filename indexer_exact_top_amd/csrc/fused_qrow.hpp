@@ -236,11 +236,23 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_sample(FusedArgs a)
                         for (int qb = 0; qb < QROW_QB; ++qb) {
                             if (qq.t[qb] >= a.T) continue;
                             float *row = a.samp + (size_t)qq.t[qb] * a.samp_cap;
+                            if (kb0 + 32 <= (int64_t)qq.L[qb]) {
+                                // registers 4g..4g+3 hold 4 consecutive keys: one 16-byte store each
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int kr = qrow_key_of(r, l);
-                                if (kb0 + kr < (int64_t)qq.L[qb])
-                                    row[vpos0 + kr] = qrow_score<C>(acc[qb][r], qq.w[qb], sc[r]);
+                                for (int g4 = 0; g4 < 4; ++g4) {
+                                    f32x4_t v;
+#pragma unroll
+                                    for (int j = 0; j < 4; ++j)
+                                        v[j] = qrow_score<C>(acc[qb][4 * g4 + j], qq.w[qb], sc[4 * g4 + j]);
+                                    *reinterpret_cast<f32x4_t *>(row + vpos0 + qrow_key_of(4 * g4, l)) = v;
+                                }
+                            } else {
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int kr = qrow_key_of(r, l);
+                                    if (kb0 + kr < (int64_t)qq.L[qb])
+                                        row[vpos0 + kr] = qrow_score<C>(acc[qb][r], qq.w[qb], sc[r]);
+                                }
                             }
                         }
                     });
@@ -584,26 +596,46 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
         }
     };
     if (!recover && n <= (uint32_t)QROW_STASH) {
+        // Gather: item i of the query's n candidates lives in the slice c with
+        // cpre[c] <= i < cpre[c + 1] (binary search in LDS), so every thread
+        // has B independent loads in flight whatever the slices' sizes.  The
+        // value range is taken on the way.
         constexpr int B = 8;
-        for (int c = wave; c < ncell; c += NT / 64) {
-            const uint32_t lo = cpre[c], cn = cpre[c + 1] - lo;
-            const Cand *cell = a.cand + ((size_t)t * ncell + c) * capH;
-            for (uint32_t i0 = 0; i0 < cn; i0 += 64 * B) {
-                Cand e[B];
+        const Cand *base = a.cand + (size_t)t * ncell * capH;
+        float mn = __builtin_inff(), mx = -__builtin_inff();
+        for (uint32_t i0 = tid; i0 < n; i0 += B * NT) {
+            Cand e[B];
 #pragma unroll
-                for (int j = 0; j < B; ++j) {
-                    const uint32_t i = i0 + j * 64 + lane;
-                    if (i < cn) e[j] = cell[i];
+            for (int j = 0; j < B; ++j) {
+                const uint32_t i = i0 + j * NT;
+                if (i < n) {
+                    int lo = 0, hi = ncell;  // cpre[lo] <= i < cpre[hi]
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (cpre[mid] <= i) lo = mid;
+                        else hi = mid;
+                    }
+                    e[j] = base[(size_t)lo * capH + (i - cpre[lo])];
                 }
+            }
 #pragma unroll
-                for (int j = 0; j < B; ++j) {
-                    const uint32_t i = i0 + j * 64 + lane;
-                    if (i < cn) sm.stash[lo + i] = make_key(e[j].val, e[j].idx);
+            for (int j = 0; j < B; ++j) {
+                const uint32_t i = i0 + j * NT;
+                if (i < n) {
+                    sm.stash[i] = make_key(e[j].val, e[j].idx);
+                    mn = fminf(mn, e[j].val);
+                    mx = fmaxf(mx, e[j].val);
                 }
             }
         }
+        mn = wave_min(mn);
+        mx = wave_max(mx);
+        if (lane == 0) {
+            sm.vmin[wave] = mn;
+            sm.vmax[wave] = mx;
+        }
         __syncthreads();
-        select_stashed<NT>(sm, n, need, emit);
+        select_stashed<NT>(sm, n, need, emit, true);
     } else if (!recover) {
         QRowSliceSrc src{a.cand + (size_t)t * ncell * capH, cpre, ncell, capH};
         exact_select<NT>(sm, src, need, emit);
