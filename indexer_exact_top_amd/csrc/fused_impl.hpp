@@ -475,10 +475,10 @@ __device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int
 
 // ---------------------------------------------------- tile staging (LDS)
 // Double-buffered key stages (and the per-key scales of FP8 keys).
-template <class C>
-struct TileBuf {
-    char k[2][C::STAGE_BYTES];
-    float scale[2][C::SCALE ? C::STAGE_KEYS : 1];
+template <class C, int NS = C::NSUB>
+struct TileBuf {  // NS 64-key tiles per stage
+    char k[2][NS * C::TILE_LDS];
+    float scale[2][C::SCALE ? NS * TILE_KEYS : 1];
 };
 
 // Per-key FP8 scales of a stage whose key bytes are copied straight to LDS:
@@ -504,8 +504,16 @@ struct ScaleStage {
 // restored afterwards).  Issued from inline assembly so that the compiler
 // does not fence later LDS accesses of other buffers on it; the caller waits
 // for completion (vmcnt) before the barrier that publishes the stage.
-__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint32_t lds_base)
+__device__ __forceinline__ void lds_dma16(const void *sbase_in, uint32_t voff, uint32_t lds_base)
 {
+    // the address is wave-uniform by construction; say so to the compiler
+    // (readfirstlane returns int: go through uint32_t, or the low word would
+    // be sign-extended into the high one)
+    const uint64_t sb = (uint64_t)sbase_in;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
+    const void *sbase = (const void *)(((uint64_t)hi << 32) | (uint64_t)lo);
+    lds_base = (uint32_t)__builtin_amdgcn_readfirstlane(lds_base);
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -552,7 +560,8 @@ struct DmaPlan {
 
     // Copies the stage starting at key0 into buffer `buf`.  Rows at or past
     // key N re-read the same chunk of the last key (never read back).
-    __device__ __forceinline__ void issue(const FusedArgs &a, TileBuf<C> &tb, int buf, int64_t key0) const
+    template <class TB>
+    __device__ __forceinline__ void issue(const FusedArgs &a, TB &tb, int buf, int64_t key0) const
     {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const uint32_t base = lds_addr(tb.k[buf]);

@@ -29,7 +29,10 @@
 
 namespace itk {
 
-constexpr int QROW_QB = 2;                      // 32-query blocks per wave
+#ifndef QROW_QBLOCKS
+#define QROW_QBLOCKS 2
+#endif
+constexpr int QROW_QB = QROW_QBLOCKS;           // 32-query blocks per wave
 constexpr int QROW_QPW = 32 * QROW_QB;          // queries per wave
 constexpr int QROW_Q = QROW_QPW * FUSED_WAVES;  // queries per workgroup
 
@@ -140,17 +143,28 @@ __device__ __forceinline__ void qrow_block_scales(float (&sc)[16], const float *
     }
 }
 
+// 64-key tiles per stage of the main scan: copied keys take stages of about
+// 64 KB per buffer (two buffers), so that each stage's copy has several
+// microseconds of MFMA work to hide behind; FP8 keys move one tile per stage
+// through registers.
+template <class C>
+constexpr int qrow_stage_tiles()
+{
+    return !C::DMA ? 1 : (C::ROWB <= 128 ? 8 : (C::ROWB <= 256 ? 4 : 2));
+}
+
 // The pipelined QRow scan: `nstages` stages of NSUB 64-key tiles, the first
 // at key `first`, `step` keys apart, keys at or beyond `key_end` skipped.
 // visit(kb0, acc, sc) is called once per computed 32-key block (wave-uniform)
 // with the block's first key and the accumulators (and FP8 scales).  Every
 // thread of the workgroup must call this.
 template <class C, int NSUB, class Visit>
-__device__ __forceinline__ void qrow_scan(const FusedArgs &a, TileBuf<C> &tb, const QRowQ<C> &qq, int64_t first,
+__device__ __forceinline__ void qrow_scan(const FusedArgs &a, TileBuf<C, NSUB> &tb, const QRowQ<C> &qq, int64_t first,
                                           int64_t step, int nstages, int64_t key_end, uint32_t wave_maxL,
                                           Visit &&visit)
 {
     static_assert(C::DMA || NSUB == 1, "FP8 staging moves one 64-key tile per stage");
+    static_assert(sizeof(tb.k[0]) == NSUB * C::TILE_LDS, "stage buffer size");
     const int64_t kend = key_end < (int64_t)wave_maxL ? key_end : (int64_t)wave_maxL;
     KStage<C> ks;
     DmaPlan<C, NSUB> dp;
@@ -208,7 +222,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_sample(FusedArgs a)
 {
-    __shared__ TileBuf<C> tb;
+    __shared__ TileBuf<C, 1> tb;
     const int l = (int)lane_id();
     int g, p;
     map_group_split(blockIdx.x, a.G, a.Ps, g, p);
@@ -404,7 +418,7 @@ __device__ __forceinline__ void qrow_collect(const f32x16_t (&acc)[QROW_QB], con
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_main(FusedArgs a)
 {
-    __shared__ TileBuf<C> tb;
+    __shared__ TileBuf<C, qrow_stage_tiles<C>()> tb;
     const int tid = threadIdx.x, l = tid & 63;
     int g, p;
     map_group_split(blockIdx.x, a.G, a.P, g, p);
@@ -432,7 +446,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_main(FusedArgs a)
     __syncthreads();
     const uint32_t gmaxL = s_max;
     if (k_hi > (int64_t)gmaxL) k_hi = gmaxL;
-    const int nstages = k_hi > k_lo ? (int)((k_hi - k_lo + C::STAGE_KEYS - 1) / C::STAGE_KEYS) : 0;
+    constexpr int SK = qrow_stage_tiles<C>() * TILE_KEYS;  // keys per stage
+    const int nstages = k_hi > k_lo ? (int)((k_hi - k_lo + SK - 1) / SK) : 0;
     // keys below kmin are valid for every lane's queries (wave-uniform)
     uint32_t kmin_l = 0xFFFFFFFFu;
 #pragma unroll
@@ -453,7 +468,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_main(FusedArgs a)
         cnt[qb] = 0;
     }
 
-    qrow_scan<C, C::NSUB>(a, tb, qq, k_lo, C::STAGE_KEYS, nstages, k_hi, gmaxL,
+    qrow_scan<C, qrow_stage_tiles<C>()>(a, tb, qq, k_lo, SK, nstages, k_hi, gmaxL,
                           [&](int64_t kb0, const f32x16_t (&acc)[QROW_QB], const float (&sc)[16]) {
                               // Block entirely below every query's length: no
                               // per-key validity test (wave-uniform choice).

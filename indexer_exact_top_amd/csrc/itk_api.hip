@@ -106,11 +106,12 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     FusedPlan p;
     p.T = T; p.H = H; p.D = D; p.N = N; p.k = k; p.qt = qt; p.kt = kt; p.flags = flags; p.HB = HB;
     if (H == 1 && qt != ITK_F32 && find_qrow_launcher(qt, kt, D, relu)) {
-        // Single head: queries are the MFMA columns (32 per block, 512 per
+        // Single head: queries are the MFMA columns (32 per block, QROW_Q per
         // workgroup); keys are split so that about 256 workgroups run.
         p.qrow = true;
-        p.G = (int32_t)ceil_div_u((uint64_t)T, 512);
-        const int64_t stage = (D * 2 <= 256) ? 128 : 64;
+        p.G = (int32_t)ceil_div_u((uint64_t)T, QROW_Q);
+        // keys per stage of the main scan (qrow_stage_tiles x 64)
+        const int64_t stage = kt == ITK_FP8_E4M3 ? 64 : (D * 2 <= 128 ? 512 : (D * 2 <= 256 ? 256 : 128));
         int P = p.G >= 256 ? 1 : (int)ceil_div_u(256, (uint64_t)p.G);
         if (P >= 8) P = (int)ceil_div_u((uint64_t)P, 8) * 8;
         const int Pmax = (int)(N / (4 * stage)) > 1 ? (int)(N / (4 * stage)) : 1;
