@@ -8,7 +8,8 @@
 // Mapping onto CDNA4 (one wavefront owns one query, FUSED_WAVES queries per
 // workgroup share every staged key tile):
 //  * contraction: v_mfma_f32_32x32x16_{bf16,f16} (v_mfma_f32_32x32x2f32 for
-//    fp32 inputs).  MFMA rows are the query's heads (one or two 32-head
+//    fp32 inputs; v_mfma_scale_f32_32x32x64_f8f6f4 when FP8 keys are scored
+//    with per-row quantized FP8 queries).  MFMA rows are the query's heads (one or two 32-head
 //    blocks), columns are 32 keys; the query's Q fragments stay in VGPRs for
 //    the whole scan, K tiles of 64 keys are staged once per workgroup into a
 //    padded, double-buffered LDS tile (FP8 keys are widened to the MFMA
@@ -27,10 +28,13 @@
 //    key passes if its bin is not below the threshold bin; passing keys are
 //    compacted with a wave ballot + popcount + lane rank into a per-wave LDS
 //    staging list that is flushed 64 entries at a time with one atomic on the
-//    row's candidate tail, and counted in the wave's LDS histogram; every few
-//    tiles the wave recomputes the threshold bin from its histogram.
-//  * select: one workgroup per row runs the exact composite-key radix
-//    refinement over the row's candidates; rows whose candidates overflowed
+//    row's candidate tail, and counted in the wave's LDS histogram; the
+//    threshold bin then moves up one bin at a time while the admitted keys
+//    strictly above it number at least k.
+//  * select: one workgroup per row gathers the row's candidates into LDS,
+//    commits every value-histogram bin above the boundary bin and settles the
+//    boundary bin exactly (ranking or composite-key radix refinement); rows
+//    whose candidates overflowed
 //    the buffer or fell short of k are re-scored from Q and K and selected
 //    exactly from the full row (recovery), so sampling never decides the
 //    result.

@@ -6,6 +6,8 @@
 //    Sec. 4.2: the fp16 ordered key shifted right by 5, 2^11 bins) and the
 //    inclusive fp32 endpoint of a coarse bin (Sec. 5.2);
 //  * a block-wide boundary search over a 2048-bin LDS histogram;
+//  * select_stashed: a value histogram over candidates held in LDS commits
+//    every bin above the boundary bin and leaves only that bin to settle;
 //  * exact_select: frontier radix refinement over the composite key.  Digits
 //    11+11+10 of the ordered fp32 key resolve the value (Sec. 5.4); three more
 //    digits of the inverted index resolve the final equal-value group in favour
@@ -22,8 +24,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int NBINS = 2048;       // one 2^11-bin histogram, reused by every round
 constexpr int STASH_CAP = 7680;   // items kept on chip (60 KB of composite keys)
-constexpr int BOUND_CAP = 1024;
-constexpr int RANK_CAP = 128;     // boundary bins up to this size are settled by ranking   // boundary-bin items kept for the final exact rounds
+constexpr int BOUND_CAP = 1024;   // boundary-bin items kept for the final exact rounds
+constexpr int RANK_CAP = 128;     // boundary bins up to this size are settled by ranking
 
 // ----------------------------------------------------------------- keys
 // Order-preserving map fp32 -> u32 (larger value -> larger key).  -0 is
