@@ -49,7 +49,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 

@@ -21,6 +21,12 @@
 namespace itk {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Word 3 of a CDNA buffer resource for raw (untyped) dword accesses: 32-bit
+// data format, no swizzle.  Accesses past the resource's byte range are
+// dropped (stores) or return zero (loads).
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
 
 constexpr int NBINS = 2048;       // one 2^11-bin histogram, reused by every round
 constexpr int STASH_CAP = 7680;   // items kept on chip (60 KB of composite keys)

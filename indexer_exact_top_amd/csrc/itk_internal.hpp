@@ -63,7 +63,7 @@ struct RaggedPlan {
     float rho = 1.5f, rho1 = 1.75f;
     int32_t force = 0;
     // workspace carve
-    size_t off_cnt = 0, off_c1 = 0, off_ep = 0, off_slices = 0, off_band = 0, bytes = 0;
+    size_t off_cnt = 0, off_ep = 0, off_slices = 0, off_band = 0, bytes = 0;
 };
 RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k);
 hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t *row_len,

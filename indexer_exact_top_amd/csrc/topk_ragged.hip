@@ -37,7 +37,6 @@ struct RaggedArgs {
     int32_t *out_idx;
     int32_t *route;
     uint32_t *cnt;   // [M][P][W] admitted per (segment, wave); may exceed subcap
-    uint32_t *c1;    // [M][P][W] values >= secondary endpoint
     float4 *ep;      // [M] {e0, e1, admit_all, 0}
     Cand *slices;    // [M][P][W][subcap]
     Cand *band;      // [M][bandcap]
@@ -62,7 +61,9 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
     __shared__ BoundaryOut b0, b1;
     __shared__ float s_e[2];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index is read into a scalar register, so that the slice
+    // address and its buffer resource below are known to be wave-uniform
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = blockIdx.x / a.P, p = blockIdx.x % a.P;
     const uint32_t L = row_length(a, r);
     const int64_t seg_lo = (int64_t)p * a.seg;
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
 
     if ((seg_lo >= (int64_t)L && p != 0) || a.force == 1) {
         if (a.force == 1 && p == 0 && tid == 0) a.ep[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (lane == 0) { a.cnt[cell] = 0u; a.c1[cell] = 0u; }
+        if (lane == 0) a.cnt[cell] = 0u;
         return;
     }
     const float *row = a.scores + (size_t)r * (size_t)a.pitch;
@@ -134,25 +135,29 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
     }
     __syncthreads();
     if (tid == 0 && p == 0) a.ep[r] = make_float4(s_e[0], s_e[1], admit_all ? 1.f : 0.f, 0.f);
-    const float e0 = s_e[0], e1 = s_e[1];
+    const float e0 = s_e[0];
 
     // ---- Phase 2: certify + collect over [seg_lo, seg_hi).
+    // The wave's slice is addressed through a buffer resource whose range is
+    // the slice: stores past its capacity are dropped by the hardware range
+    // check.  The count keeps growing, and a count above the capacity sends
+    // the row to the exact route, which ignores the slice.
     Cand *slice = a.slices + cell * (size_t)a.subcap;
-    const uint32_t subcap = (uint32_t)a.subcap;
+    const __amdgpu_buffer_rsrc_t srd =
+        __builtin_amdgcn_make_buffer_rsrc(slice, 0, (int)(a.subcap * (int)sizeof(Cand)), BUF_RSRC_WORD3);
     uint32_t cnt = 0;   // wave-uniform: admitted so far
-    uint32_t c1v = 0;   // per lane: values >= e1
-    // One score: C(tau1) is counted per lane; an admitted score takes the next
-    // slot of the wave's slice (ballot + lane rank).  Past the slice capacity
-    // the last slot is overwritten: the count keeps growing, and a count above
-    // the capacity sends the row to the exact route, which ignores the slice.
-    // Positions past the segment hold NaN, which no comparison admits.
+    // One score: an admitted score takes the next slot of the wave's slice
+    // (compare mask + lane rank).  Positions past the segment hold NaN, which
+    // no comparison admits.  The secondary count C(tau1) is not taken here:
+    // the finisher needs it only for an underfilled row, and then takes it in
+    // its band pass.
     auto classify = [&](uint32_t i, float x) {
-        c1v += x >= e1 ? 1u : 0u;
         const uint64_t m0 = __builtin_amdgcn_fcmpf(x, e0, 3);  // ordered >=, as a lane mask
         if (x >= e0) {
             const uint32_t slot =
                 __builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, cnt));
-            slice[min(slot, subcap - 1u)] = Cand{i, x};
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{i, __float_as_uint(x)}, srd, slot * (uint32_t)sizeof(Cand),
+                                                  0, 0);
         }
         cnt += (uint32_t)__builtin_popcountll(m0);
     };
@@ -188,11 +193,7 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
             }
         }
     }
-    const uint32_t c1 = lane_value(wave_incl_sum(c1v), 63);
-    if (lane == 0) {
-        a.cnt[cell] = cnt;
-        a.c1[cell] = c1;
-    }
+    if (lane == 0) a.cnt[cell] = cnt;
 }
 
 // Items of a row's candidate slices (and band slice), for exact_select.
@@ -325,8 +326,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
 {
     __shared__ SelectSmem sm;
-    __shared__ uint32_t s_c0, s_c1, s_ovf, s_band_n;
-    __shared__ int s_route;
+    __shared__ uint32_t s_c0, s_ovf, s_band_n;
     __shared__ uint32_t cpre[RAG_MAX_CELLS + 1];
 
     const int tid = threadIdx.x;
@@ -338,7 +338,6 @@ __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
     const float4 ep = a.ep[r];
     const bool has_cell = tid < ncells;
     const uint32_t my_cnt = has_cell ? a.cnt[cell0 + tid] : 0u;
-    const uint32_t my_c1 = has_cell ? a.c1[cell0 + tid] : 0u;
     const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
     int32_t *out = a.out_idx + (size_t)r * a.k;
     for (uint32_t i = need + tid; i < (uint32_t)a.k; i += NT) out[i] = -1;
@@ -346,30 +345,26 @@ __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
         if (tid == 0 && a.route) a.route[r] = ROUTE_ALL;
         return;
     }
-    if (tid == 0) { s_c0 = 0; s_c1 = 0; s_ovf = 0; s_band_n = 0; }
+    if (tid == 0) { s_c0 = 0; s_ovf = 0; s_band_n = 0; }
     __syncthreads();
     for (int c = tid; c < ncells; c += NT) {
         const uint32_t n = c == tid ? my_cnt : a.cnt[cell0 + c];
         atomicAdd(&s_c0, n);
-        atomicAdd(&s_c1, c == tid ? my_c1 : a.c1[cell0 + c]);
         if (n > (uint32_t)a.subcap) atomicOr(&s_ovf, 1u);
     }
     __syncthreads();
     const float *row = a.scores + (size_t)r * (size_t)a.pitch;
-    if (tid == 0) {
-        const uint32_t C0 = s_c0, C1 = s_c1;
-        int route = ROUTE_EXACT;
-        if (a.force == 1 || s_ovf) route = ROUTE_EXACT;
-        else if (C0 >= need && a.force != 2) route = ep.z != 0.f ? ROUTE_ALL : ROUTE_SAMPLE;
-        else if (C1 >= need && C1 - C0 <= (uint32_t)a.bandcap) route = ROUTE_BAND;
-        s_route = route;
-    }
-    __syncthreads();
-    const int route = s_route;
+    const uint32_t C0 = s_c0;
+    int route = ROUTE_BAND;  // underfilled, or the sample route forced off
+    if (a.force == 1 || s_ovf) route = ROUTE_EXACT;
+    else if (C0 >= need && a.force != 2) route = ep.z != 0.f ? ROUTE_ALL : ROUTE_SAMPLE;
 
     if (route == ROUTE_BAND) {
         // Second traversal: append the values admitted by the secondary
-        // endpoint but not by the primary one.
+        // endpoint but not by the primary one, and count them all, so that
+        // C(tau1) = C0 + band count.  The band route holds when C(tau1)
+        // reaches the quota and the band fits its slice; otherwise the row
+        // takes the exact route.
         Cand *band = a.band + (size_t)r * a.bandcap;
         const float e0 = ep.x, e1 = ep.y;
         RowSrc rs{row, L, vec != 0};
@@ -379,6 +374,7 @@ __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
             if (in && slot < (uint32_t)a.bandcap) band[slot] = Cand{i, x};
         });
         __syncthreads();
+        if (C0 + s_band_n < need || s_band_n > (uint32_t)a.bandcap) route = ROUTE_EXACT;
     }
 
     auto emit = [&](uint32_t slot, uint64_t K) {
@@ -390,8 +386,8 @@ __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
     } else {
         SliceSrc src{a.slices + cell0 * (size_t)a.subcap, a.cnt + cell0, ncells, (uint32_t)a.subcap,
                      a.band + (size_t)r * a.bandcap, route == ROUTE_BAND ? min(s_band_n, (uint32_t)a.bandcap) : 0u};
-        // the slices hold at most C0 (route 1) or C1 (route 2) entries
-        const uint32_t bound = route == ROUTE_BAND ? s_c1 : s_c0;
+        // the slices and the band slice hold at most this many entries
+        const uint32_t bound = route == ROUTE_BAND ? C0 + s_band_n : C0;
         if (bound <= (uint32_t)STASH_CAP && ncells <= RAG_MAX_CELLS) {
             const uint32_t n = gather_candidates(src, sm, cpre);
             select_stashed<NT>(sm, n, need, emit, true);
@@ -409,11 +405,14 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     const Knobs &kn = knobs();
     RaggedPlan p;
     p.M = M; p.pitch = pitch; p.k = k;
-    // about 512 workgroups, and segments of at most 32768 scores (128 KB), so
-    // that long rows do not serialize on one workgroup
+    // about 512 workgroups, and below 1024 rows segments of at most 32768
+    // scores (128 KB), so that long rows do not serialize on one workgroup
     int target = ceil_div_i(512, M);
     const int by_len = ceil_div_i(pitch > 0 ? pitch : 1, RAG_SEG_MAX);
-    if (target < by_len) target = by_len;
+    // From 1024 rows on, one workgroup per row already fills the chip, and
+    // every extra segment repeats the row's view pass (measured on 1024 rows
+    // of 8K-128K scores: one segment per row 107 us, four 118 us).
+    if (M < 1024 && target < by_len) target = by_len;
     if (target < 1) target = 1;
     if (target > 16) target = 16;
     if (kn.splits > 0) target = kn.splits;
@@ -438,7 +437,6 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     const size_t cells = (size_t)M * p.P * RAG_WAVES;
     size_t off = 0;
     p.off_cnt = off; off = align256(off + cells * 4);
-    p.off_c1 = off; off = align256(off + cells * 4);
     p.off_ep = off; off = align256(off + (size_t)M * 16);
     p.off_slices = off; off = align256(off + cells * (size_t)p.subcap * sizeof(Cand));
     p.off_band = off; off = align256(off + (size_t)M * p.bandcap * sizeof(Cand));
@@ -460,7 +458,6 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
     const RouteSink &rs = route_sink();
     a.route = (rs.ptr && rs.rows >= p.M) ? rs.ptr : nullptr;
     a.cnt = reinterpret_cast<uint32_t *>(w + p.off_cnt);
-    a.c1 = reinterpret_cast<uint32_t *>(w + p.off_c1);
     a.ep = reinterpret_cast<float4 *>(w + p.off_ep);
     a.slices = reinterpret_cast<Cand *>(w + p.off_slices);
     a.band = reinterpret_cast<Cand *>(w + p.off_band);
