@@ -44,7 +44,8 @@ constexpr int RAG_WAVES = RAG_THREADS / 64;
 #ifndef RAG_SEG_MAX
 #define RAG_SEG_MAX 32768
 #endif
-constexpr int RAG_MAX_CELLS = 64;  // (segment, wave) cells per row that the finisher gathers on chip
+constexpr int RAG_MAX_SPLITS = 64;                      // segments per row chosen by the planner
+constexpr int RAG_MAX_CELLS = RAG_MAX_SPLITS * RAG_WAVES; // (segment, wave) cells the finisher gathers on chip
 // Ragged finisher: one workgroup per row, 1024 threads for up to 255 rows
 // (latency-bound), 512 from 256 rows on (several rows per CU).
 constexpr int FIN_THREADS = 1024;

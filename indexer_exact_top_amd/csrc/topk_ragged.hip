@@ -251,65 +251,80 @@ enum { ROUTE_SAMPLE = 1, ROUTE_BAND = 2, ROUTE_EXACT = 3, ROUTE_ALL = 4 };
 
 // Copies every candidate of a row (slices in cell order, then the band
 // slice) into the on-chip stash as composite keys; returns the count.  The
-// caller guarantees that the count fits STASH_CAP.  Cell offsets come from a
-// wave prefix sum over the per-cell counts; then each wave copies whole
-// cells, with all of a lane's loads issued before any is consumed, so the
-// copy costs about one memory round trip instead of one per item.
-__device__ uint32_t gather_candidates(const SliceSrc &src, SelectSmem &sm, uint32_t *cpre)
+// caller guarantees that the count fits STASH_CAP and that cpre holds the
+// prefix of the per-cell counts (cpre[c] <= item < cpre[c + 1] for the items
+// of cell c).  With at most two cells per wave, each wave copies whole cells
+// (all of a lane's loads of a cell issued before any is consumed).  With more
+// cells, item i is located by a fixed-step binary search over cpre in LDS, so
+// that every thread keeps B independent loads in flight whatever the cells'
+// sizes (measured on one row of 2^20 scores in 64 segments: 4.2 us against
+// 16 round trips for the per-wave copy; the per-wave copy is about 1 us
+// faster with 8 segments).  The value range is taken on the way
+// (select_stashed reads it).
+__device__ uint32_t gather_candidates(const SliceSrc &src, const uint32_t *cpre, SelectSmem &sm)
 {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < 64) {
-        uint32_t carry = 0;
-        for (int base = 0; base < src.ncells; base += 64) {
-            const int c = base + lane;
-            const uint32_t v = c < src.ncells ? min(src.cnt[c], src.subcap) : 0u;
-            const uint32_t incl = wave_incl_sum(v);
-            if (c < src.ncells) cpre[c + 1] = carry + incl;
-            carry += lane_value(incl, 63);
-        }
-        if (tid == 0) cpre[0] = 0;
-    }
-    __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nt = blockDim.x, nw = nt >> 6;
     const uint32_t nslice = cpre[src.ncells], total = nslice + src.band_n;
-    constexpr int B = 8;  // loads in flight per lane
-    // value range of the gathered items, per wave (select_stashed reads it)
+    constexpr int B = 8;  // loads in flight per thread
     float mn = __builtin_inff(), mx = -__builtin_inff();
-    for (int c = wave; c < src.ncells; c += blockDim.x >> 6) {
-        const uint32_t lo = cpre[c], n = cpre[c + 1] - lo;
-        const Cand *cell = src.slices + (size_t)c * src.subcap;
-        for (uint32_t i0 = 0; i0 < n; i0 += 64 * B) {
-            Cand e[B];
+    auto put = [&](uint32_t i, const Cand &e) {
+        sm.stash[i] = make_key(e.val, e.idx);
+        mn = fminf(mn, e.val);
+        mx = fmaxf(mx, e.val);
+    };
+    if (src.ncells <= 2 * nw) {
+        for (int c = wave; c < src.ncells; c += nw) {
+            const uint32_t lo = cpre[c], n = cpre[c + 1] - lo;
+            const Cand *cell = src.slices + (size_t)c * src.subcap;
+            for (uint32_t i0 = 0; i0 < n; i0 += 64 * B) {
+                Cand e[B];
 #pragma unroll
-            for (int j = 0; j < B; ++j) {
-                const uint32_t i = i0 + j * 64 + lane;
-                if (i < n) e[j] = cell[i];
-            }
+                for (int j = 0; j < B; ++j) {
+                    const uint32_t i = i0 + j * 64 + lane;
+                    if (i < n) e[j] = cell[i];
+                }
 #pragma unroll
-            for (int j = 0; j < B; ++j) {
-                const uint32_t i = i0 + j * 64 + lane;
-                if (i < n) {
-                    sm.stash[lo + i] = make_key(e[j].val, e[j].idx);
-                    mn = fminf(mn, e[j].val);
-                    mx = fmaxf(mx, e[j].val);
+                for (int j = 0; j < B; ++j) {
+                    const uint32_t i = i0 + j * 64 + lane;
+                    if (i < n) put(lo + i, e[j]);
                 }
             }
         }
+    } else {
+        for (uint32_t i0 = tid; i0 < nslice; i0 += B * nt) {
+            Cand e[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const uint32_t i = i0 + j * nt;
+                if (i < nslice) {
+                    // largest lo < ncells with cpre[lo] <= i, in a fixed
+                    // number of steps, so that the B searches interleave
+                    // (every index read stays below RAG_MAX_CELLS)
+                    int lo = 0;
+#pragma unroll
+                    for (int step = RAG_MAX_CELLS / 2; step >= 1; step >>= 1)
+                        if (lo + step < src.ncells && cpre[lo + step] <= i) lo += step;
+                    e[j] = src.slices[(size_t)lo * src.subcap + (i - cpre[lo])];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const uint32_t i = i0 + j * nt;
+                if (i < nslice) put(i, e[j]);
+            }
+        }
     }
-    for (uint32_t i0 = 0; i0 < src.band_n; i0 += blockDim.x * B) {
+    for (uint32_t i0 = tid; i0 < src.band_n; i0 += B * nt) {
         Cand e[B];
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            const uint32_t i = i0 + j * blockDim.x + tid;
+            const uint32_t i = i0 + j * nt;
             if (i < src.band_n) e[j] = src.band[i];
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            const uint32_t i = i0 + j * blockDim.x + tid;
-            if (i < src.band_n) {
-                sm.stash[nslice + i] = make_key(e[j].val, e[j].idx);
-                mn = fminf(mn, e[j].val);
-                mx = fmaxf(mx, e[j].val);
-            }
+            const uint32_t i = i0 + j * nt;
+            if (i < src.band_n) put(nslice + i, e[j]);
         }
     }
     mn = wave_min(mn);
@@ -325,8 +340,10 @@ __device__ uint32_t gather_candidates(const SliceSrc &src, SelectSmem &sm, uint3
 template <int NT>
 __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
 {
+    static_assert(RAG_MAX_CELLS <= NT, "one cell per thread in the count prefix");
     __shared__ SelectSmem sm;
     __shared__ uint32_t s_c0, s_ovf, s_band_n;
+    __shared__ uint32_t s_wsum[NT / 64];
     __shared__ uint32_t cpre[RAG_MAX_CELLS + 1];
 
     const int tid = threadIdx.x;
@@ -347,12 +364,26 @@ __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
     }
     if (tid == 0) { s_c0 = 0; s_ovf = 0; s_band_n = 0; }
     __syncthreads();
+    // Total admitted count C0 and the overflow flag; with at most one cell
+    // per thread, also the prefix of the stored (capped) counts, cpre.
+    const bool on_chip_cells = ncells <= RAG_MAX_CELLS;
     for (int c = tid; c < ncells; c += NT) {
         const uint32_t n = c == tid ? my_cnt : a.cnt[cell0 + c];
         atomicAdd(&s_c0, n);
         if (n > (uint32_t)a.subcap) atomicOr(&s_ovf, 1u);
     }
+    uint32_t incl = 0;
+    if (on_chip_cells) {
+        incl = wave_incl_sum(min(my_cnt, (uint32_t)a.subcap));
+        if ((tid & 63) == 63) s_wsum[tid >> 6] = incl;
+    }
     __syncthreads();
+    if (on_chip_cells) {
+        uint32_t off = 0;
+        for (int w = 0; w < (tid >> 6); ++w) off += s_wsum[w];
+        if (has_cell) cpre[tid + 1] = off + incl;
+        if (tid == 0) cpre[0] = 0;
+    }
     const float *row = a.scores + (size_t)r * (size_t)a.pitch;
     const uint32_t C0 = s_c0;
     int route = ROUTE_BAND;  // underfilled, or the sample route forced off
@@ -388,8 +419,9 @@ __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
                      a.band + (size_t)r * a.bandcap, route == ROUTE_BAND ? min(s_band_n, (uint32_t)a.bandcap) : 0u};
         // the slices and the band slice hold at most this many entries
         const uint32_t bound = route == ROUTE_BAND ? C0 + s_band_n : C0;
-        if (bound <= (uint32_t)STASH_CAP && ncells <= RAG_MAX_CELLS) {
-            const uint32_t n = gather_candidates(src, sm, cpre);
+        if (bound <= (uint32_t)STASH_CAP && on_chip_cells) {
+            __syncthreads();  // cpre complete
+            const uint32_t n = gather_candidates(src, cpre, sm);
             select_stashed<NT>(sm, n, need, emit, true);
         } else {
             exact_select<NT>(sm, src, need, emit);
@@ -405,8 +437,10 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     const Knobs &kn = knobs();
     RaggedPlan p;
     p.M = M; p.pitch = pitch; p.k = k;
-    // about 512 workgroups, and below 1024 rows segments of at most 32768
-    // scores (128 KB), so that long rows do not serialize on one workgroup
+    // about 512 workgroups (up to RAG_MAX_SPLITS segments per row, so that a
+    // few long rows, as in decoding, still spread over the chip), and below
+    // 1024 rows segments of at most 32768 scores (128 KB), so that long rows
+    // do not serialize on one workgroup
     int target = ceil_div_i(512, M);
     const int by_len = ceil_div_i(pitch > 0 ? pitch : 1, RAG_SEG_MAX);
     // From 1024 rows on, one workgroup per row already fills the chip, and
@@ -414,7 +448,7 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     // of 8K-128K scores: one segment per row 107 us, four 118 us).
     if (M < 1024 && target < by_len) target = by_len;
     if (target < 1) target = 1;
-    if (target > 16) target = 16;
+    if (target > RAG_MAX_SPLITS) target = RAG_MAX_SPLITS;
     if (kn.splits > 0) target = kn.splits;
     int64_t seg = (pitch + target - 1) / target;
     seg = ((seg + 1023) / 1024) * 1024;
@@ -424,10 +458,24 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     int s = pitch >= 262144 ? 128 : 64;
     if (kn.sample_stride > 0) s = kn.sample_stride;
     p.view_blocks = s;
-    p.rho = kn.rho > 0.f ? kn.rho : 1.5f;
-    p.rho1 = kn.rho1 > 0.f ? kn.rho1 : 1.75f;
+    // Primary and secondary rank multiples: 1.5 and 1.75 as long as the
+    // view's sample rank q0 = rho*k/s is at least 32; below that the
+    // rank estimate is too coarse (on exchangeable rows the count admitted
+    // by the q-th view value is about Gamma(q, 1) * L / n_a, so q = 24 at
+    // s = 128, k = 2048 underfills about 4% of rows), and rho is raised to
+    // 32*s/k (rho1 = 7/6 rho), which keeps the underfill rate near 3e-4.
+    const float rho_floor = 32.f * (float)s / (float)(k > 0 ? k : 1);
+    const float rho_auto = rho_floor > 1.5f ? rho_floor : 1.5f;
+    p.rho = kn.rho > 0.f ? kn.rho : rho_auto;
+    p.rho1 = kn.rho1 > 0.f ? kn.rho1 : rho_auto * (7.f / 6.f);
     if (p.rho1 < p.rho) p.rho1 = p.rho;
-    int segcap = (int)(2.0 * p.rho1 * k + 0.5);
+    // Each segment can hold twice the row's expected secondary count (any
+    // one segment may hold all of a row's top values); past 16 segments per
+    // row the per-segment share shrinks in proportion, which bounds the
+    // workspace at 32 times the row's expected count.
+    double segcap_d = 2.0 * p.rho1 * k;
+    if (p.P > 16) segcap_d *= 16.0 / p.P;
+    int segcap = (int)(segcap_d + 0.5);
     if (segcap < 2048) segcap = 2048;
     if (kn.capacity > 0) segcap = kn.capacity;
     p.subcap = (segcap + RAG_WAVES - 1) / RAG_WAVES;
