@@ -100,11 +100,14 @@ def test_config3_sampled_rows(itk):
     print(f"config3 (T=64) recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
 
 
-def test_config4_sampled_rows(itk):
-    case = synth.fused_config(4, T=16)
+@pytest.mark.parametrize("T,rows", [(16, [0, 9]), (1, [0])])
+def test_config4_sampled_rows(itk, T, rows):
+    """The 1M-key FP8 workload with 16 queries, and with one (a decoding
+    step: all 256 workgroups come from key splits)."""
+    case = synth.fused_config(4, T=T)
     idx, sc, routes = _run(itk, case, routes=True)
-    rec = check_fused_rows(case, [0, 9], idx, sc, min_recall=0.95)
-    print(f"config4 (T=16) recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
+    rec = check_fused_rows(case, rows, idx, sc, min_recall=0.95)
+    print(f"config4 (T={T}) recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
 
 
 @pytest.mark.parametrize("knobs", [dict(force_route=1), dict(capacity=1024, rho=50.0), dict(splits=8),
