@@ -836,14 +836,19 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
 }
 
 // Equal-width bin mapping from the sampled score range (m = NBINS bins).
+// Called by every lane of a wave: the Ps per-split ranges are read by the
+// lanes in parallel (a one-query decode call has 256 splits; read one after
+// the other they took most of the histogram pass).
 __device__ __forceinline__ float4 bin_params(const FusedArgs &a, int t)
 {
     float mn = __builtin_inff(), mx = -__builtin_inff();
-    for (int p = 0; p < a.Ps; ++p) {
+    for (int p = (int)lane_id(); p < a.Ps; p += 64) {
         const float2 v = a.mm[(size_t)t * a.Ps + p];
         mn = fminf(mn, v.x);
         mx = fmaxf(mx, v.y);
     }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
     const float delta = (float)NBINS / (mx - mn);
     const bool ok = (mx > mn) && __builtin_isfinite(delta) && delta > 0.f && __builtin_isfinite(mn);
     return ok ? make_float4(-mn * delta, delta, 0.f, 0.f) : make_float4(0.f, 0.f, 1.f, 0.f);

@@ -212,11 +212,13 @@ struct BoundaryOut {
     uint32_t total;  // items in all bins
 };
 
-// d = max{b : sum_{b' >= b} hist[b'] >= quota}.  When quota exceeds the
-// total, d = 0 and above + eq == total.  Block of NT threads; `scan` holds
-// NT/64 words.  Ends with a barrier; the result is in `out` for every thread.
-template <int NT>
-__device__ void find_boundary(const uint32_t *hist, uint32_t quota, uint32_t *scan, BoundaryOut *out)
+// d = max{b : sum_{b' >= b} hist[b'] >= quota}, for NQ quotas at once (one
+// pass over the histogram).  When a quota exceeds the total, d = 0 and
+// above + eq == total.  Block of NT threads; `scan` holds NT/64 words.  Ends
+// with a barrier; the results are in `out` for every thread.
+template <int NT, int NQ>
+__device__ void find_boundaries(const uint32_t *hist, const uint32_t (&quota)[NQ], uint32_t *scan,
+                                BoundaryOut *const (&out)[NQ])
 {
     constexpr int PER = NBINS / NT;
     const int tid = threadIdx.x;
@@ -238,27 +240,38 @@ __device__ void find_boundary(const uint32_t *hist, uint32_t quota, uint32_t *sc
         if (w > wave) above_waves += scan[w];
     }
     const uint32_t excl = incl - s + above_waves;  // items in bins above this thread's bins
-    if (tid == 0 && total < quota) {
-        out->digit = 0;
-        out->above = total - hist[0];
-        out->eq = hist[0];
-        out->total = total;
-    }
-    if (excl < quota && excl + s >= quota) {
-        uint32_t cum = excl;
 #pragma unroll
-        for (int i = PER - 1; i >= 0; --i) {
-            if (cum + loc[i] >= quota) {
-                out->digit = (uint32_t)(tid * PER + i);
-                out->above = cum;
-                out->eq = loc[i];
-                out->total = total;
-                break;
+    for (int q = 0; q < NQ; ++q) {
+        if (tid == 0 && total < quota[q]) {
+            out[q]->digit = 0;
+            out[q]->above = total - hist[0];
+            out[q]->eq = hist[0];
+            out[q]->total = total;
+        }
+        if (excl < quota[q] && excl + s >= quota[q]) {
+            uint32_t cum = excl;
+#pragma unroll
+            for (int i = PER - 1; i >= 0; --i) {
+                if (cum + loc[i] >= quota[q]) {
+                    out[q]->digit = (uint32_t)(tid * PER + i);
+                    out[q]->above = cum;
+                    out[q]->eq = loc[i];
+                    out[q]->total = total;
+                    break;
+                }
+                cum += loc[i];
             }
-            cum += loc[i];
         }
     }
     __syncthreads();
+}
+
+template <int NT>
+__device__ void find_boundary(const uint32_t *hist, uint32_t quota, uint32_t *scan, BoundaryOut *out)
+{
+    const uint32_t q[1] = {quota};
+    BoundaryOut *const o[1] = {out};
+    find_boundaries<NT, 1>(hist, q, scan, o);
 }
 
 // --------------------------------------------------------- exact select

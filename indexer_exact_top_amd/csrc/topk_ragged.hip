@@ -126,8 +126,9 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
     const uint32_t q1 = (uint32_t)ceil((double)a.rho1 * a.k * frac);
     const bool admit_all = (n_a < q1) || q0 == 0u || ((double)a.rho1 * a.k >= (double)L);
     if (!admit_all) {
-        find_boundary<RAG_THREADS>(hist, q0, scan_tmp, &b0);
-        find_boundary<RAG_THREADS>(hist, q1, scan_tmp, &b1);
+        const uint32_t qs[2] = {q0, q1};
+        BoundaryOut *const bs[2] = {&b0, &b1};
+        find_boundaries<RAG_THREADS, 2>(hist, qs, scan_tmp, bs);
     }
     if (wave < 2) {  // wave 0: primary endpoint, wave 1: secondary
         const float e = admit_all ? -__builtin_inff() : coarse_endpoint_wave(wave == 0 ? b0.digit : b1.digit);
