@@ -162,8 +162,8 @@ struct FusedArgs {
     uint32_t *hist;    // [T][NBINS] sample histogram
     uint32_t *tail;    // [T] candidates appended (may exceed cap)
     Cand *cand;        // [T][cap] (head rows) or [T][P][capS] (single head)
+    float *samp;       // [T][samp_cap] scores of the sampled view (both paths)
     // single-head (query-column) path
-    float *samp;       // [T][samp_cap] scores of the sampled view
     float *gate;       // [T] admission gate (score space)
     uint32_t *qcnt;    // [T][P] candidates per (query, key split); may exceed capS
     int64_t N, span, span_s, samp_cap;
@@ -822,11 +822,18 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
     QFrags<C> qf;
     if (active) qf.load(a, t);
     float mn = __builtin_inff(), mx = -__builtin_inff();
+    // When the plan gives room for it, the view's scores are also stored
+    // (sampled tile j of the row at samp[t][64 j ...], NaN past the row), so
+    // that pass B bins them without scoring the view again.
+    const int64_t phase = g % a.sample_tiles;
+    float *srow = a.samp ? a.samp + (size_t)(active ? t : 0) * a.samp_cap : nullptr;
     scan_tiles<C, 1>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, it.end, active, L, [&](int64_t key0, float s) {
-        if (key0 + lane < (int64_t)L) {
+        const bool valid = key0 + lane < (int64_t)L;
+        if (valid) {
             mn = fminf(mn, s);
             mx = fmaxf(mx, s);
         }
+        if (srow) srow[((key0 / TILE_KEYS - phase) / a.sample_tiles) * TILE_KEYS + lane] = valid ? s : __builtin_nanf("");
     });
     if (active) {
         mn = wave_min(mn);
@@ -860,6 +867,9 @@ __device__ __forceinline__ uint32_t bin_of(float b)
 }
 
 // ---------------------------------------- sample pass B: sample histogram
+// Bins the view scores that pass A stored (the same tiles of the same split,
+// so every score is counted once), or, when the plan stores no view (a view
+// larger than the candidate buffer), scores the view again.
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
 {
@@ -879,13 +889,36 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
     }
     const uint32_t maxL = group_max_len(a, g);
     const SampleIter it = sample_iter(a, g, p, maxL);
-    QFrags<C> qf;
-    if (active) qf.load(a, t);
     // a degenerate sampled range leaves the gate open: nothing to count
     const bool count = active && bp.z == 0.f;
-    scan_tiles<C, 1>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, it.end, count, L, [&](int64_t key0, float s) {
-        if (key0 + lane < (int64_t)L) atomicAdd(&whist[wave][bin_of(fmaf(s, bp.y, bp.x))], 1u);
-    });
+    if (!a.samp) {  // workgroup-uniform
+        QFrags<C> qf;
+        if (active) qf.load(a, t);
+        scan_tiles<C, 1>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, it.end, count, L,
+                         [&](int64_t key0, float s) {
+                             if (key0 + lane < (int64_t)L) atomicAdd(&whist[wave][bin_of(fmaf(s, bp.y, bp.x))], 1u);
+                         });
+    } else if (count) {
+        // the tiles pass A visited: first_key + i * stride below min(end, L)
+        const int64_t kend = it.end < (int64_t)L ? it.end : (int64_t)L;
+        const int64_t phase = g % a.sample_tiles;
+        const float *srow = a.samp + (size_t)t * a.samp_cap;
+        int n = 0;
+        if (it.first_key >= 0 && it.first_key < kend)
+            n = (int)((kend - it.first_key + it.stride_keys - 1) / it.stride_keys);
+        if (n > it.ntiles) n = it.ntiles;
+        const int64_t j0 = (it.first_key / TILE_KEYS - phase) / a.sample_tiles;  // first sampled tile's slot
+        constexpr int B = 8;  // loads in flight per lane
+        for (int i0 = 0; i0 < n; i0 += B) {
+            float v[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j)
+                v[j] = i0 + j < n ? srow[(j0 + i0 + j) * TILE_KEYS + lane] : __builtin_nanf("");
+#pragma unroll
+            for (int j = 0; j < B; ++j)
+                if (v[j] == v[j]) atomicAdd(&whist[wave][bin_of(fmaf(v[j], bp.y, bp.x))], 1u);
+        }
+    }
     __syncthreads();
     if (count) {
         for (int i = lane; i < NBINS; i += 64) {

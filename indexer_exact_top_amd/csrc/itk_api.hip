@@ -178,6 +178,11 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     if (cap < need_all) cap = need_all;
     p.cap = cap;
     p.force = kn.force_route;
+    // Pass A stores the view's scores (at most ceil(tiles / stride) tiles per
+    // row) when they take no more bytes than the candidate buffer, which
+    // keeps the workspace O(T k); a longer view is scored again by pass B.
+    p.samp_cap = (int64_t)ceil_div_u((uint64_t)ntiles, (uint64_t)st) * TILE_KEYS;
+    if (p.samp_cap > 2 * (int64_t)cap) p.samp_cap = 0;
     size_t off = 0;
     p.off_param = off; off = align256(off + (size_t)T * sizeof(float4));
     p.off_mm = off; off = align256(off + (size_t)T * p.Ps * sizeof(float2));
@@ -185,6 +190,7 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     p.off_tail = off; off = align256(off + (size_t)T * sizeof(uint32_t));
     p.off_gate = off; off = align256(off + (size_t)T * sizeof(int32_t));
     p.off_cand = off; off = align256(off + (size_t)T * cap * sizeof(Cand));
+    p.off_samp = off; off = align256(off + (size_t)T * p.samp_cap * sizeof(float));
     p.bytes = off;
     *out = p;
     return ITK_OK;
@@ -208,13 +214,13 @@ hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const 
     a.N = p.N; a.span = p.span; a.span_s = p.span_s;
     a.T = p.T; a.H = p.H; a.k = p.k; a.cap = p.cap; a.G = p.G; a.P = p.P; a.Ps = p.Ps;
     a.sample_tiles = p.sample_tiles; a.force = p.force; a.rho = p.rho;
-    a.samp = nullptr; a.gate = nullptr; a.qcnt = nullptr; a.samp_cap = 0; a.capS = 0;
+    a.samp = p.samp_cap > 0 ? reinterpret_cast<float *>(w + p.off_samp) : nullptr;
+    a.samp_cap = p.samp_cap;
+    a.gate = nullptr; a.qcnt = nullptr; a.capS = 0;
     if (p.qrow) {
-        a.samp = reinterpret_cast<float *>(w + p.off_samp);
         a.gate = reinterpret_cast<float *>(w + p.off_gate);
         a.qcnt = reinterpret_cast<uint32_t *>(w + p.off_qcnt);
         a.cand = reinterpret_cast<Cand *>(w + p.off_cand);
-        a.samp_cap = p.samp_cap;
         a.capS = p.capS;
         FusedLauncher fn = find_qrow_launcher(p.qt, p.kt, p.D, !(p.flags & ITK_FLAG_NO_RELU));
         if (!fn) return hipErrorInvalidValue;

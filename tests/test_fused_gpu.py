@@ -79,8 +79,13 @@ def test_relu_zero_rows_recover_exactly(itk):
 
 
 @pytest.mark.parametrize("knobs", [dict(force_route=1), dict(capacity=2048, rho=50.0), dict(splits=8),
-                                   dict(sample_stride=1, rho=1.0), dict(splits=3, sample_stride=5)])
+                                   dict(sample_stride=1, rho=1.0), dict(splits=3, sample_stride=5),
+                                   dict(sample_stride=10)])
 def test_routes_and_plans_give_identical_sets(itk, knobs):
+    """Forced routes and other plans give the same index sets.  The default
+    plan and sample_stride=10 store the view's scores for the histogram pass;
+    sample_stride=1 and 5 give views longer than the candidate buffer, which
+    the histogram pass scores again."""
     case = synth.gen_fused(16, 64, 128, 40000, 512, q_dtype=synth.BF16, k_dtype=synth.BF16,
                            kv_len=np.arange(16) * 1000 + 25000, seed=44)
     base, bsc, _ = _run(itk, case)
