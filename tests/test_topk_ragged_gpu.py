@@ -97,14 +97,17 @@ def test_repeat_deterministic(itk):
         assert np.array_equal(np.sort(a, axis=1), np.sort(b, axis=1))
 
 
-@pytest.mark.parametrize("M,family", [(1, "config2"), (3, "config2"), (2, "descending")])
-def test_decode_rows_of_one_million(itk, M, family):
+@pytest.mark.parametrize("M,family,k", [(1, "config2", 2048), (3, "config2", 2048), (2, "descending", 2048),
+                                        (2, "gaussian", 64)])
+def test_decode_rows_of_one_million(itk, M, family, k):
     """A few rows of 2^20 scores (decoding against a 1M context): the planner
     spreads each row over up to 64 segments; a descending row puts every top
-    value in one segment, overflows its slices and takes the exact route."""
+    value in one segment, overflows its slices and takes the exact route.
+    With k = 64 the view's sample rank would be below 32 at rho = 1.5, so
+    the planner raises rho to 32 s / k = 64."""
     pitch = 1 << 20
     lens = np.array([pitch, pitch - 12345, pitch - 1][:M], dtype=np.int32)
-    case = synth.gen_ragged(M, pitch, 2048, lens=lens, seed=900 + M, family=family)
+    case = synth.gen_ragged(M, pitch, k, lens=lens, seed=900 + M, family=family)
     out, routes = _run(itk, case, routes=True)
     check_ragged_exact(case, out)
     if family == "descending":
