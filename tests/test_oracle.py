@@ -64,6 +64,35 @@ def _all_rows(case):
 
 
 # ------------------------------------------------------------ score pins
+def test_score_against_python_loops():
+    """Eq. (1) written out as float64 loops on tiny signed inputs, with some
+    negative head weights and causal lengths below N: every score of every
+    valid key, to fp32 rounding of the row's magnitude."""
+    rng = np.random.default_rng(12)
+    T, H, D, N = 3, 3, 8, 40
+    q = rng.standard_normal((T, H, D))
+    kk = rng.standard_normal((N, D))
+    W = rng.random((T, H)) - 0.25
+    kv = [40, 23, 1]
+    c = _case(T, H, D, N, 5, q=q, kk=kk, W=W, kv_len=kv)
+    qf, kf, wf = (c.q_bits.astype(np.float64), c.k_bits.astype(np.float64), c.W.astype(np.float64))
+    for t in range(T):
+        got = oracle.fused_score_row(c, t)
+        assert got.shape == (kv[t],)
+        ref = []
+        for j in range(kv[t]):
+            acc = 0.0
+            for h in range(H):
+                dot = 0.0
+                for d in range(D):
+                    dot += qf[t, h, d] * kf[j, d]
+                acc += wf[t, h] * max(dot, 0.0)
+            ref.append(acc)
+        ref = np.array(ref)
+        scale = sum(abs(wf[t, h]) * np.abs(qf[t, h]) @ np.abs(kf[j]) for h in range(H) for j in range(kv[t]))
+        assert np.max(np.abs(got - ref)) <= 1e-6 * scale / kv[t] + 1e-30
+
+
 def test_inner_product_equals_numpy_matmul():
     c = _case(5, 1, 24, 37, 4, W=np.ones((5, 1)), no_relu=True)
     q = c.q_bits.reshape(5, 24).astype(np.float64)
