@@ -35,7 +35,7 @@ FP8_E4M3_MAX = 448.0
 
 __all__ = [
     "F32", "BF16", "F16", "FP8_E4M3", "FLAG_NO_RELU", "FusedCase", "RaggedCase",
-    "gen_fused", "gen_ragged", "fused_config", "ragged_config", "CONFIGS",
+    "gen_fused", "gen_ragged", "fused_config", "ragged_config", "csa_chunk", "CONFIGS",
     "encode", "decode_reference_free",
 ]
 
@@ -280,6 +280,22 @@ def ragged_config(seed: int = 202, M: int = 64, pitch: int = 131072, k: int = 20
     lens = rng.integers(8192, pitch + 1, size=M).astype(np.int32)
     return gen_ragged(M, pitch, k, lens=lens, seed=seed + 1, family="config2",
                       name="cfg2_standalone_ragged")
+
+
+def csa_chunk(S: int, chunk: int, *, m: int = 4, k: int = 2048, H: int = 64, D: int = 128,
+              start: Optional[int] = None, seed: int = 606) -> FusedCase:
+    """One query chunk of a compressed-key (CSA) indexer step: a sequence of
+    S tokens whose keys are compressed m to 1 (S/m key rows), the chunk's
+    ``chunk`` query tokens starting at token ``start`` (default: the last
+    chunk), H indexer heads of dimension D, bf16 Q and K ~ N(0,1)/sqrt(D),
+    W ~ U(0,1)/H.  Token t sees the compressed keys whose m tokens are all at
+    or before it: kv_len = floor((t + 1) / m), so the first m - 1 tokens of a
+    sequence see no key (StreamIndex summary: V4-style CSA, H_I = 64, m = 4)."""
+    N = S // m
+    t0 = S - chunk if start is None else start
+    kv = (np.arange(t0, t0 + chunk, dtype=np.int64) + 1) // m
+    return gen_fused(chunk, H, D, N, k, q_dtype=BF16, k_dtype=BF16, kv_len=kv.astype(np.int32),
+                     seed=seed, name=f"csa_chunk_S{S}_m{m}")
 
 
 CONFIGS = {

@@ -194,3 +194,16 @@ def test_fp8_scoring_config4_sampled_rows(itk):
     idx, sc, routes = _run(itk, case, routes=True)
     rec = check_fp8_score_rows(case, [0, 64, 127], idx, sc, min_recall=0.8)
     print(f"config4 fp8 scoring: recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
+
+
+@pytest.mark.parametrize("S,chunk,start,rows", [(16384, 64, 0, range(64)), (65536, 64, 32768, [0, 31, 63]),
+                                                (65536, 32, 65536 - 32, [0, 31])])
+def test_compressed_key_chunks(itk, S, chunk, start, rows):
+    """Compressed-key (CSA, m = 4) query chunks: token t sees floor((t+1)/4)
+    compressed keys.  The first chunk of a sequence has rows with no key and
+    rows with fewer keys than k (all valid keys returned, the rest padded);
+    later chunks select 2048 of 8K-16K keys."""
+    case = synth.csa_chunk(S, chunk, start=start)
+    idx, sc, routes = _run(itk, case, routes=True)
+    rec = check_fused_rows(case, list(rows), idx, sc, min_recall=0.99)
+    print(f"csa S={S} start={start} recall min {rec.min():.4f} routes {np.bincount(routes).tolist()}")
