@@ -39,7 +39,11 @@ def check_fused_rows(case, rows, gpu_idx, gpu_score, tol=None, min_recall=None):
             continue
         kth = o_val[r, need - 1]
         ora_sel = oracle.fused_scores_at(case, np.full(need, t), sel)
-        denom = np.maximum(np.abs(ora_sel), abs(kth))
+        # relative to max(|own score|, |k-th score|, 1e-3 |top score|): the
+        # last term keeps near-zero scores of rows whose k-th score is 0
+        # (fewer valid keys than k, ReLU zeros) at the row's scale, where fp32
+        # accumulation-order differences are absolute, not relative
+        denom = np.maximum(np.maximum(np.abs(ora_sel), abs(kth)), 1e-3 * abs(o_val[r, 0]))
         denom = np.where(denom > 0, denom, 1.0)
         err = np.abs(gs[:need].astype(np.float64) - ora_sel) / denom
         assert err.max() <= tol, f"row {t}: score error {err.max():.3g} > {tol}"

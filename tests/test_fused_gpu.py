@@ -207,3 +207,17 @@ def test_compressed_key_chunks(itk, S, chunk, start, rows):
     idx, sc, routes = _run(itk, case, routes=True)
     rec = check_fused_rows(case, list(rows), idx, sc, min_recall=0.99)
     print(f"csa S={S} start={start} recall min {rec.min():.4f} routes {np.bincount(routes).tolist()}")
+
+
+def test_rows_whose_kth_score_is_zero(itk):
+    """fp16, three heads, D = 256: rows with fewer valid keys than k select
+    every key, including keys whose heads are all cut by the ReLU (score 0)
+    and keys with scores far below the row's top, so the k-th score is 0 and
+    the tolerance falls back to the row's scale (found by a randomized
+    sweep; row 22 has 1279 keys for k = 2032)."""
+    kv = [368, 9013, 50511, 48233, 24873, 50511, 50511, 24726, 28579, 19988, 50511, 18789, 25830, 19206,
+          29445, 25884, 20406, 30345, 50511, 45480, 38152, 26032, 1279]
+    case = synth.gen_fused(23, 3, 256, 50511, 2032, q_dtype=synth.F16, k_dtype=synth.F16,
+                           kv_len=np.array(kv, np.int32), seed=116552435)
+    idx, sc, _ = _run(itk, case)
+    check_fused_rows(case, range(case.T), idx, sc, min_recall=0.99)
