@@ -567,8 +567,10 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
 {
     constexpr int NT = SEL_THREADS;
     __shared__ SelectSmemT<QROW_STASH> sm;
+    static_assert(2 * QROW_MAX_SPLITS <= NT, "one slice per thread in the count prefix");
     __shared__ uint32_t cpre[2 * QROW_MAX_SPLITS + 1];
     __shared__ uint32_t s_ovf;
+    __shared__ uint32_t s_wsum[NT / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t = blockIdx.x;
     const uint32_t L = kv_length(a, t);
@@ -585,20 +587,20 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
         if (tid == 0 && a.route) a.route[t] = 4;
         return;
     }
-    // slice counts -> prefix (cpre) and overflow flag
+    // slice counts -> prefix (cpre) and overflow flag: one slice per thread,
+    // all counts loaded at once, then a block-wide prefix sum
     if (tid == 0) s_ovf = 0;
-    __syncthreads();
     const uint32_t *cnt = a.qcnt + (size_t)t * ncell;
-    if (tid < 64) {
-        uint32_t carry = 0;
-        for (int base = 0; base < ncell; base += 64) {
-            const int c = base + lane;
-            const uint32_t raw = c < ncell ? cnt[c] : 0u;
-            if (raw > capH) atomicOr(&s_ovf, 1u);
-            const uint32_t incl = wave_incl_sum(min(raw, capH));
-            if (c < ncell) cpre[c + 1] = carry + incl;
-            carry += lane_value(incl, 63);
-        }
+    const uint32_t raw = tid < ncell ? cnt[tid] : 0u;
+    __syncthreads();
+    if (raw > capH) atomicOr(&s_ovf, 1u);
+    const uint32_t incl = wave_incl_sum(min(raw, capH));
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    {
+        uint32_t off = 0;
+        for (int w = 0; w < wave; ++w) off += s_wsum[w];
+        if (tid < ncell) cpre[tid + 1] = off + incl;
         if (tid == 0) cpre[0] = 0;
     }
     __syncthreads();
@@ -624,12 +626,13 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
             for (int j = 0; j < B; ++j) {
                 const uint32_t i = i0 + j * NT;
                 if (i < n) {
-                    int lo = 0, hi = ncell;  // cpre[lo] <= i < cpre[hi]
-                    while (hi - lo > 1) {
-                        const int mid = (lo + hi) >> 1;
-                        if (cpre[mid] <= i) lo = mid;
-                        else hi = mid;
-                    }
+                    // largest lo < ncell with cpre[lo] <= i, in a fixed number
+                    // of steps, so that the B searches of a thread interleave
+                    // (every index read stays below 2 * QROW_MAX_SPLITS)
+                    int lo = 0;
+#pragma unroll
+                    for (int step = QROW_MAX_SPLITS; step >= 1; step >>= 1)
+                        if (lo + step < ncell && cpre[lo + step] <= i) lo += step;
                     e[j] = base[(size_t)lo * capH + (i - cpre[lo])];
                 }
             }
