@@ -20,8 +20,10 @@
 //    are combined with one cross-lane exchange, leaving lane l with the score
 //    of key tile_start + l.
 //  * sample -> filter -> refresh -> select (LiteTopK Sec. 3.2): a tile-strided
-//    view of each row is scored first (two light passes: score range, then an
-//    equal-width histogram of m = 2048 bins over [s_min, s_max]); the
+//    view of each row is scored first (two light passes: the score range,
+//    with the view's scores stored when they fit the candidate buffer's
+//    bytes, then an equal-width histogram of m = 2048 bins over
+//    [s_min, s_max] from the stored scores, or from a second scoring); the
 //    threshold bin starts at the bin of the sample's rank-q score, q sized
 //    for rho * k of the row (the rank calibration of the Sample-Guided paper,
 //    Sec. 4.2).  In the scan, bin = floor((s - s_min) * delta) is one FMA; a

@@ -11,16 +11,17 @@
 //                   inclusive fp32 endpoints (Sec. 5.2).  Phase 2: one pass
 //                   over the segment with 16-byte non-temporal loads (the
 //                   first batch issued before phase 1, later ones double-
-//                   buffered) compares each value with the endpoints
+//                   buffered) compares each value with the primary endpoint
 //                   (Sec. 5.3); admitted values are appended to a per-wave
 //                   slice whose slots come from a compare mask + popcount +
-//                   lane rank (no atomics), and the secondary count is kept
-//                   per lane and summed once per wave.
+//                   lane rank (no atomics).
 //  k_ragged_finish  one workgroup per row.  Sums the per-wave counts and
 //                   picks the route: certified primary, band pass (Sec. 4.3
-//                   "Underfilled views"), or the exact route over the whole
-//                   row (Table 2).  Then exact_select refines the frontier
-//                   (Sec. 5.4) and writes the indices.
+//                   "Underfilled views"; the pass also counts the values
+//                   between the endpoints, which gives C(tau1)), or the exact
+//                   route over the whole row (Table 2).  Then the candidates
+//                   are gathered on chip and refined (Sec. 5.4), and the
+//                   indices written.
 //
 // The view samples 16 consecutive elements (one 64-byte segment) out of every
 // 16*s: 1/s of the row like a single-element stride, but every sampled byte
