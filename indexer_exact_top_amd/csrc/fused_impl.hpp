@@ -439,43 +439,74 @@ __device__ __forceinline__ void sched_block()
     }
 }
 
-// Same scores with B fragments read straight from global K (recovery path).
+// B fragments of one 32-key block read straight from global K (recovery
+// route and the few-query scan): lane l holds key column l % 32 at the
+// k-slice l / 32 of every k-step.  All of a block's loads are issued by
+// load() before any is used; FP8 keys are kept as loaded and widened (like
+// the staged copy) only in score(), so that load() never waits for data.
 template <class C>
-__device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int64_t key0)
-{
-    const int l = (int)lane_id();
-    float part[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        f32x16_t acc[C::HB];
-#pragma unroll
-        for (int hb = 0; hb < C::HB; ++hb) acc[hb] = f32x16_t{};
-        const int64_t key = key0 + kb * 32 + (l & 31);
+struct GlobalBlock {
+    static constexpr bool WIDEN = C::KT == ITK_FP8_E4M3 && C::MT != M_FP8;
+    typename C::frag b[WIDEN ? 1 : C::KS];
+    u32x2_t raw[WIDEN ? C::KS : 1];
+    // bytes per lane that a block's loads hold
+    static constexpr int BYTES = WIDEN ? C::KS * 8 : C::KS * (int)sizeof(typename C::frag);
+    __device__ __forceinline__ void load(const FusedArgs &a, int64_t kb0)
+    {
+        const int l = (int)lane_id();
+        const int64_t key = kb0 + (l & 31);
         const bool ok = key < a.N;
         const char *krow = static_cast<const char *>(a.K) + (size_t)(ok ? key : 0) * C::D * C::kbytes;
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) {
-            typename C::frag b;
             if constexpr (C::MT == M_F32) {
-                b = ok ? reinterpret_cast<const float *>(krow)[kk * 2 + (l >> 5)] : 0.f;
+                b[kk] = ok ? reinterpret_cast<const float *>(krow)[kk * 2 + (l >> 5)] : 0.f;
             } else if constexpr (C::MT == M_FP8) {
                 const int d0 = kk * 64 + 32 * (l >> 5);
-                b = ok ? *reinterpret_cast<const u32x8_t *>(krow + d0) : u32x8_t{};
-            } else if constexpr (C::KT == ITK_FP8_E4M3) {
+                b[kk] = ok ? *reinterpret_cast<const u32x8_t *>(krow + d0) : u32x8_t{};
+            } else if constexpr (WIDEN) {
                 const int d0 = kk * 16 + 8 * (l >> 5);
-                const u32x2_t raw = ok ? *reinterpret_cast<const u32x2_t *>(krow + d0) : u32x2_t{0u, 0u};
-                const u32x2_t lo = fp8x4_widen<C::MT>(raw[0]), hi = fp8x4_widen<C::MT>(raw[1]);
-                b = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+                raw[kk] = ok ? *reinterpret_cast<const u32x2_t *>(krow + d0) : u32x2_t{0u, 0u};
             } else {
                 const int d0 = kk * 16 + 8 * (l >> 5);
-                b = ok ? *reinterpret_cast<const u32x4_t *>(krow + d0 * 2) : u32x4_t{0u, 0u, 0u, 0u};
+                b[kk] = ok ? *reinterpret_cast<const u32x4_t *>(krow + d0 * 2) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    // The block's weighted, ReLU'd head sum per lane (half of a key's score).
+    __device__ __forceinline__ float score(const QFrags<C> &qf) const
+    {
+        f32x16_t acc[C::HB];
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb) acc[hb] = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk) {
+            typename C::frag f;
+            if constexpr (WIDEN) {
+                const u32x2_t lo = fp8x4_widen<C::MT>(raw[kk][0]), hi = fp8x4_widen<C::MT>(raw[kk][1]);
+                f = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+            } else {
+                f = b[kk];
             }
 #pragma unroll
-            for (int hb = 0; hb < C::HB; ++hb) acc[hb] = mfma32<C::MT>(qf.q[hb][kk], b, acc[hb]);
+            for (int hb = 0; hb < C::HB; ++hb) acc[hb] = mfma32<C::MT>(qf.q[hb][kk], f, acc[hb]);
         }
-        part[kb] = reduce_block<C>(acc, qf.w);
+        return reduce_block<C>(acc, qf.w);
     }
-    return combine_halves(part[0], part[1]);
+};
+
+// Same scores with B fragments read straight from global K (recovery path).
+// One block's fragments are live at a time (the select kernel that runs it
+// has little register room).
+template <class C>
+__device__ float tile_scores_global(const QFrags<C> &qf, const FusedArgs &a, int64_t key0)
+{
+    GlobalBlock<C> gb;
+    gb.load(a, key0);
+    const float p0 = gb.score(qf);
+    gb.load(a, key0 + 32);
+    const float p1 = gb.score(qf);
+    return combine_halves(p0, p1);
 }
 
 // ---------------------------------------------------- tile staging (LDS)
@@ -1039,6 +1070,118 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
     if (active && own_row && lane == 0) a.tail[t] = tail_reg;
 }
 
+// ---------------------------------------------- main pass, few queries
+// Few-query variant of the main scan (decoding): every wave works alone on a
+// key range of one query (a.P ranges per query, a.span keys each), with the
+// B fragments read straight from global K as in the recovery route, so there
+// are no shared key stages and no barriers, and a single query keeps every
+// SIMD of the chip busy instead of one wave per workgroup.  The scores are
+// bit-identical to the staged scan's (same MFMA order); gate, binning, LDS
+// histogram, refresh and compaction are those of k_fused_main, per wave.
+template <class C>
+__global__ __launch_bounds__(FUSED_THREADS) void k_fused_main_kp(FusedArgs a)
+{
+    __shared__ uint32_t whist_all[FUSED_WAVES][NBINS];
+    __shared__ Cand stage_all[FUSED_WAVES][128];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (a.force == 1) return;  // every row takes the re-scoring route
+    const int64_t gw = (int64_t)blockIdx.x * FUSED_WAVES + wave;
+    const int t = (int)(gw / a.P);
+    const int p = (int)(gw % a.P);
+    if (t >= a.T) return;  // no barriers below: a wave may leave on its own
+    const uint32_t L = kv_length(a, t);
+    const int64_t k_lo = (int64_t)p * a.span;
+    const int64_t k_hi = k_lo + a.span < (int64_t)L ? k_lo + a.span : (int64_t)L;
+    if (k_hi <= k_lo) return;
+    uint32_t *whist = whist_all[wave];
+    Cand *stage = stage_all[wave];
+    for (int i = lane; i < NBINS; i += 64) whist[i] = 0u;
+
+    float off = 0.f, delta = 0.f;
+    int gate_bin = 0;
+    float gate_f = -__builtin_inff();
+    {
+        const float4 bp = a.param[t];
+        const RowSample rs = row_sample(a, t / FUSED_WAVES, L, bp.z != 0.f);
+        if (!rs.admit_all) {
+            off = bp.x;
+            delta = bp.y;
+            const int b = wave_top_bin(a.hist + (size_t)t * NBINS, rs.q0);
+            gate_bin = b > 0 ? b : 0;
+            gate_f = gate_bin > 0 ? (float)gate_bin : -__builtin_inff();
+        }
+    }
+    QFrags<C> qf;
+    qf.load(a, t);
+    uint32_t stage_n = 0, inrange = 0, at_gate = 0;
+    Cand *cand = a.cand + (size_t)t * a.cap;
+    const uint32_t cap = (uint32_t)a.cap;
+    const uint32_t kq = (uint32_t)a.k;
+    const bool refresh = delta > 0.f;
+    auto flush = [&](uint32_t n) {
+        uint32_t slot = 0;
+        if (lane == 0) slot = atomicAdd(&a.tail[t], n);
+        slot = lane_value(slot, 0);
+        if ((uint32_t)lane < n && slot + lane < cap) cand[slot + lane] = stage[lane];
+    };
+    // Blocks of 32 keys alternate between two register sets, so that the
+    // loads of the next block are in flight while the current one is scored,
+    // when a block's fragments take at most 32 registers (otherwise one set).
+    constexpr bool PF = GlobalBlock<C>::BYTES <= 128;
+    GlobalBlock<C> ga, gb;
+    ga.load(a, k_lo);
+    for (int64_t key0 = k_lo; key0 < k_hi; key0 += TILE_KEYS) {
+        float p0, p1;
+        if constexpr (PF) {
+            gb.load(a, key0 + 32);
+            p0 = ga.score(qf);
+            if (key0 + TILE_KEYS < k_hi) ga.load(a, key0 + TILE_KEYS);
+            p1 = gb.score(qf);
+        } else {
+            p0 = ga.score(qf);
+            ga.load(a, key0 + 32);
+            p1 = ga.score(qf);
+            if (key0 + TILE_KEYS < k_hi) ga.load(a, key0 + TILE_KEYS);
+        }
+        float s = combine_halves(p0, p1);
+        const int64_t key = key0 + lane;
+        const bool valid = key < k_hi;
+        if constexpr (C::SCALE) s *= valid ? a.k_scale[key] : 1.f;
+        const float b = fmaf(s, delta, off);
+        const bool pass = valid && b >= gate_f;
+        const uint64_t m = __ballot(pass);
+        if (m) {
+            const uint32_t bin = bin_of(b);
+            const uint32_t pos = stage_n + lanes_below(m);
+            if (pass) {
+                atomicAdd(&whist[bin], 1u);
+                stage[pos] = Cand{(uint32_t)key, s};
+            }
+            const uint32_t n = (uint32_t)__popcll(m);
+            stage_n += n;
+            inrange += n;
+            at_gate += (uint32_t)__popcll(__ballot(pass && bin == (uint32_t)gate_bin));
+            if (stage_n >= 64u) {
+                flush(64u);
+                const bool mv = (uint32_t)lane < stage_n - 64u;
+                Cand e;
+                if (mv) e = stage[64 + lane];
+                if (mv) stage[lane] = e;
+                stage_n -= 64u;
+            }
+            if (refresh && inrange - at_gate >= kq && gate_bin < NBINS - 1) {
+                do {
+                    inrange -= at_gate;
+                    ++gate_bin;
+                    at_gate = whist[gate_bin];
+                } while (inrange - at_gate >= kq && gate_bin < NBINS - 1);
+                gate_f = (float)gate_bin;
+            }
+        }
+    }
+    if (stage_n) flush(stage_n);
+}
+
 // ------------------------------------------- select (+ recovery) per row
 struct CandSrc {
     const Cand *c;
@@ -1169,7 +1312,11 @@ hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         StageTimer st(ST_F_MAIN, stream);
-        hipLaunchKernelGGL(k_fused_main<C>, dim3(p.G * p.P), dim3(FUSED_THREADS), 0, stream, a);
+        if (p.kp)
+            hipLaunchKernelGGL(k_fused_main_kp<C>, dim3((unsigned)((int64_t)p.T * p.P / FUSED_WAVES)),
+                               dim3(FUSED_THREADS), 0, stream, a);
+        else
+            hipLaunchKernelGGL(k_fused_main<C>, dim3(p.G * p.P), dim3(FUSED_THREADS), 0, stream, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {

@@ -165,6 +165,20 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     P = (int)ceil_div_u((uint64_t)N, (uint64_t)span);
     p.P = P; p.span = span;
     p.Ps = P; p.span_s = span;
+    // Few queries: one key range per wave in the main pass (the sample
+    // passes keep the workgroup splits above).  P is a multiple of the waves
+    // per workgroup, so that the grid is whole; ranges past N stay empty.
+    if (T <= KP_MAX_T && kn.splits == 0) {
+        int64_t Pw = (int64_t)ceil_div_u((uint64_t)KP_WAVES, (uint64_t)T);
+        int64_t span_w = (int64_t)ceil_div_u((uint64_t)N, (uint64_t)Pw);
+        span_w = (int64_t)ceil_div_u((uint64_t)span_w, TILE_KEYS) * TILE_KEYS;
+        if (span_w < 4 * TILE_KEYS) span_w = 4 * TILE_KEYS;
+        Pw = (int64_t)ceil_div_u((uint64_t)N, (uint64_t)span_w);
+        Pw = (int64_t)ceil_div_u((uint64_t)Pw, FUSED_WAVES) * FUSED_WAVES;
+        p.kp = true;
+        p.P = (int32_t)Pw;
+        p.span = span_w;
+    }
     const int64_t ntiles = (int64_t)ceil_div_u((uint64_t)N, TILE_KEYS);
     int st = (int)((ntiles + 31) / 32);
     if (st < 1) st = 1;

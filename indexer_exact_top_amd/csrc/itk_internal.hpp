@@ -81,6 +81,14 @@ constexpr int TILE_KEYS = 64;
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_THREADS_HR = 512;
 constexpr int QROW_MAX_SPLITS = 256;  // single-head path: key splits per query
+// Head-rows path with at most KP_MAX_T queries: the main pass runs one key
+// range per wave, about KP_WAVES waves in all (two per SIMD).  Measured on
+// 2^20 FP8 keys, H = 64, D = 128: one query 59 us against 72 us with the
+// staged scan; two or four queries were slower than the staged scan (the
+// per-lane 8-byte fragment loads from global memory, 32 rows per
+// instruction, cost more L1 cycles than the MFMAs they feed).
+constexpr int KP_MAX_T = 1;
+constexpr int KP_WAVES = 2048;
 
 struct FusedPlan {
     int32_t T = 0, H = 0, D = 0, k = 0;
@@ -98,6 +106,7 @@ struct FusedPlan {
     int32_t cap = 0;         // candidates per row
     int32_t force = 0;
     bool qrow = false;       // single-head path: queries as MFMA columns
+    bool kp = false;         // head rows, few queries: main pass with one key range per wave
     int32_t capS = 0;        // single head: candidates per (query, key split)
     int64_t samp_cap = 0;    // single head: stored view scores per query
     size_t off_param = 0, off_mm = 0, off_hist = 0, off_tail = 0, off_gate = 0, off_cand = 0;

@@ -221,3 +221,35 @@ def test_rows_whose_kth_score_is_zero(itk):
                            kv_len=np.array(kv, np.int32), seed=116552435)
     idx, sc, _ = _run(itk, case)
     check_fused_rows(case, range(case.T), idx, sc, min_recall=0.99)
+
+
+@pytest.mark.parametrize("qt,kt,H,D,T", [(synth.BF16, synth.BF16, 64, 128, 1), (synth.BF16, synth.FP8_E4M3, 64, 128, 3),
+                                         (synth.F16, synth.F16, 20, 256, 1), (synth.F16, synth.FP8_E4M3, 33, 64, 1),
+                                         (synth.F32, synth.F32, 8, 64, 1), (synth.BF16, synth.BF16, 64, 128, 4)])
+def test_few_queries_key_parallel(itk, qt, kt, H, D, T):
+    """One query: the main pass gives each wave its own key range (B
+    fragments from global memory); three and four queries take the staged
+    scan.  Lengths include 0, 1, a partial tile and fewer keys than k; the
+    sets equal the forced re-scoring route's."""
+    N = 70000
+    kv = np.array([N, 1, 0, 4000, 131][:T], dtype=np.int32)
+    kv[0] = N
+    case = synth.gen_fused(T, H, D, N, 1024, q_dtype=qt, k_dtype=kt, kv_len=kv, seed=60 + T)
+    idx, sc, routes = _run(itk, case, routes=True)
+    check_fused_rows(case, range(T), idx, sc, min_recall=0.99)
+    itk.set_plan_opts(force_route=1)
+    try:
+        ridx, rsc, _ = _run(itk, case)
+    finally:
+        itk.reset_plan_opts()
+    assert np.array_equal(np.sort(idx, axis=1), np.sort(ridx, axis=1))
+    assert np.array_equal(np.sort(sc, axis=1), np.sort(rsc, axis=1))
+    print("few-query routes", routes.tolist())
+
+
+def test_few_queries_fp8_scoring(itk):
+    case = synth.gen_fused(1, 64, 128, 50000, 2048, q_dtype=synth.BF16, k_dtype=synth.FP8_E4M3,
+                           kv_len=np.array([30001], np.int32), seed=71)
+    case.flags |= itk.FLAG_FP8_SCORE
+    idx, sc, _ = _run(itk, case)
+    check_fp8_score_rows(case, [0], idx, sc)
