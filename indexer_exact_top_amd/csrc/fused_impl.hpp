@@ -1070,6 +1070,50 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
     if (active && own_row && lane == 0) a.tail[t] = tail_reg;
 }
 
+// One 32-key block copied by one wave into its own LDS rows (few-query
+// scan): each load instruction reads whole 16-byte chunks of consecutive key
+// rows (RC lanes per row), so the global reads are coalesced; store() writes
+// them (FP8 keys widened) into the padded row layout of the staged tiles, so
+// that block_mfma reads the B fragments as in the staged scan.
+template <class C>
+struct WaveBlock {
+    static constexpr int RAW = C::D * C::kbytes;  // global bytes per key row
+    static constexpr int RC = RAW / 16;           // 16-byte chunks per row
+    static constexpr int RPI = 64 / RC;           // rows per load instruction
+    static constexpr int NI = 32 / RPI;           // load instructions per block
+    static constexpr bool WIDEN = C::KT == ITK_FP8_E4M3 && C::MT != M_FP8;
+    static constexpr bool OK = RC >= 1 && RC <= 16 && 64 % RC == 0 && 32 * C::ROWP * FUSED_WAVES <= 80 * 1024;
+    u32x4_t v[OK ? NI : 1];
+    __device__ __forceinline__ void load(const FusedArgs &a, int64_t kb0)
+    {
+        const int l = (int)lane_id();
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int64_t key = kb0 + i * RPI + l / RC;
+            const bool ok = key < a.N;
+            v[i] = ok ? *reinterpret_cast<const u32x4_t *>(static_cast<const char *>(a.K) + (size_t)key * RAW +
+                                                           (l % RC) * 16)
+                      : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(char *base) const
+    {
+        const int l = (int)lane_id();
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            char *dst = base + (i * RPI + l / RC) * C::ROWP;
+            if constexpr (WIDEN) {
+                const u32x2_t w0 = fp8x4_widen<C::MT>(v[i][0]), w1 = fp8x4_widen<C::MT>(v[i][1]);
+                const u32x2_t w2 = fp8x4_widen<C::MT>(v[i][2]), w3 = fp8x4_widen<C::MT>(v[i][3]);
+                *reinterpret_cast<u32x4_t *>(dst + (l % RC) * 32) = u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+                *reinterpret_cast<u32x4_t *>(dst + (l % RC) * 32 + 16) = u32x4_t{w2[0], w2[1], w3[0], w3[1]};
+            } else {
+                *reinterpret_cast<u32x4_t *>(dst + (l % RC) * 16) = v[i];
+            }
+        }
+    }
+};
+
 // ---------------------------------------------- main pass, few queries
 // Few-query variant of the main scan (decoding): every wave works alone on a
 // key range of one query (a.P ranges per query, a.span keys each), with the
@@ -1083,6 +1127,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main_kp(FusedArgs a)
 {
     __shared__ uint32_t whist_all[FUSED_WAVES][NBINS];
     __shared__ Cand stage_all[FUSED_WAVES][128];
+    constexpr bool LDSB = WaveBlock<C>::OK;
+    __shared__ __attribute__((aligned(16))) char kblk_all[LDSB ? FUSED_WAVES * 32 * C::ROWP : 16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if (a.force == 1) return;  // every row takes the re-scoring route
     const int64_t gw = (int64_t)blockIdx.x * FUSED_WAVES + wave;
@@ -1124,15 +1170,36 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main_kp(FusedArgs a)
         slot = lane_value(slot, 0);
         if ((uint32_t)lane < n && slot + lane < cap) cand[slot + lane] = stage[lane];
     };
-    // Blocks of 32 keys alternate between two register sets, so that the
-    // loads of the next block are in flight while the current one is scored,
-    // when a block's fragments take at most 32 registers (otherwise one set).
+    // Blocks of 32 keys: with coalesced row loads into two register sets
+    // (two blocks in flight) and the wave's own LDS rows (LDSB), else with
+    // B fragments loaded directly, two register sets when a block's
+    // fragments take at most 32 registers.
     constexpr bool PF = GlobalBlock<C>::BYTES <= 128;
     GlobalBlock<C> ga, gb;
-    ga.load(a, k_lo);
+    WaveBlock<C> wa, wbk;
+    char *wl = kblk_all + (LDSB ? wave * 32 * C::ROWP : 0);
+    const int boff = bfrag_lane_off<C>();
+    if constexpr (LDSB) {
+        wa.load(a, k_lo);
+        wbk.load(a, k_lo + 32);
+    } else {
+        ga.load(a, k_lo);
+    }
     for (int64_t key0 = k_lo; key0 < k_hi; key0 += TILE_KEYS) {
         float p0, p1;
-        if constexpr (PF) {
+        if constexpr (LDSB) {
+            // LDS accesses of one wave complete in order, so each block's
+            // fragment reads are done before the next block's rows land
+            f32x16_t acc[C::HB];
+            wa.store(wl);
+            if (key0 + TILE_KEYS < k_hi) wa.load(a, key0 + TILE_KEYS);
+            block_mfma<C>(acc, qf, wl + boff);
+            p0 = reduce_block<C>(acc, qf.w);
+            wbk.store(wl);
+            if (key0 + TILE_KEYS + 32 < k_hi) wbk.load(a, key0 + TILE_KEYS + 32);
+            block_mfma<C>(acc, qf, wl + boff);
+            p1 = reduce_block<C>(acc, qf.w);
+        } else if constexpr (PF) {
             gb.load(a, key0 + 32);
             p0 = ga.score(qf);
             if (key0 + TILE_KEYS < k_hi) ga.load(a, key0 + TILE_KEYS);
