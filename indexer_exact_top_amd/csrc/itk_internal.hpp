@@ -83,11 +83,11 @@ constexpr int SEL_THREADS_HR = 512;
 constexpr int QROW_MAX_SPLITS = 256;  // single-head path: key splits per query
 // Head-rows path with at most KP_MAX_T queries: the main pass runs one key
 // range per wave, about KP_WAVES waves in all (two per SIMD).  Measured on
-// 2^20 FP8 keys, H = 64, D = 128: one query 59 us against 72 us with the
-// staged scan; two or four queries were slower than the staged scan (the
-// per-lane 8-byte fragment loads from global memory, 32 rows per
-// instruction, cost more L1 cycles than the MFMAs they feed).
-constexpr int KP_MAX_T = 1;
+// 2^20 FP8 keys, H = 64, D = 128 (main pass): one query 48 us against 72 us
+// with the staged scan, two 66 against 79 us; four (104 against 94 us) and
+// eight (182 against 145 us) are faster staged, where eight queries share
+// each staged key tile.
+constexpr int KP_MAX_T = 2;
 constexpr int KP_WAVES = 2048;
 
 struct FusedPlan {

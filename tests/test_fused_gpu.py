@@ -224,11 +224,12 @@ def test_rows_whose_kth_score_is_zero(itk):
 
 
 @pytest.mark.parametrize("qt,kt,H,D,T", [(synth.BF16, synth.BF16, 64, 128, 1), (synth.BF16, synth.FP8_E4M3, 64, 128, 3),
-                                         (synth.F16, synth.F16, 20, 256, 1), (synth.F16, synth.FP8_E4M3, 33, 64, 1),
+                                         (synth.F16, synth.F16, 20, 256, 1), (synth.F16, synth.FP8_E4M3, 33, 64, 2),
                                          (synth.F32, synth.F32, 8, 64, 1), (synth.BF16, synth.BF16, 64, 128, 4)])
 def test_few_queries_key_parallel(itk, qt, kt, H, D, T):
-    """One query: the main pass gives each wave its own key range (B
-    fragments from global memory); three and four queries take the staged
+    """One or two queries: the main pass gives each wave its own key range
+    (coalesced row loads into the wave's own LDS rows, or B fragments from
+    global memory for wide rows); three and four queries take the staged
     scan.  Lengths include 0, 1, a partial tile and fewer keys than k; the
     sets equal the forced re-scoring route's."""
     N = 70000
