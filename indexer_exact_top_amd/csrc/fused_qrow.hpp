@@ -293,18 +293,36 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_gate(FusedArgs a)
     }
     const float *row = a.samp + (size_t)t * a.samp_cap;
     const uint32_t n = rs.n_a;
+    // A view of at most VR * NT scores is loaded once, all of a thread's
+    // loads in flight together, and kept in registers for both passes.
+    constexpr int VR = 32;
+    const bool resident = n <= (uint32_t)(VR * NT);
+    float vr[VR];
     float mn = __builtin_inff(), mx = -__builtin_inff();
-    for (uint32_t i0 = tid; i0 < n; i0 += 8 * NT) {
-        float v[8];
+    if (resident) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t i = i0 + j * NT;
-            v[j] = i < n ? row[i] : __builtin_nanf("");
+        for (int j = 0; j < VR; ++j) {
+            const uint32_t i = tid + j * NT;
+            vr[j] = i < n ? row[i] : __builtin_nanf("");
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            mn = fminf(mn, v[j]);
-            mx = fmaxf(mx, v[j]);
+        for (int j = 0; j < VR; ++j) {
+            mn = fminf(mn, vr[j]);
+            mx = fmaxf(mx, vr[j]);
+        }
+    } else {
+        for (uint32_t i0 = tid; i0 < n; i0 += 8 * NT) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t i = i0 + j * NT;
+                v[j] = i < n ? row[i] : __builtin_nanf("");
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                mn = fminf(mn, v[j]);
+                mx = fmaxf(mx, v[j]);
+            }
         }
     }
     mn = wave_min(mn);
@@ -327,17 +345,23 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_gate(FusedArgs a)
         if (tid == 0) a.gate[t] = -__builtin_inff();
         return;
     }
-    for (uint32_t i0 = tid; i0 < n; i0 += 8 * NT) {
-        float v[8];
+    auto bin_add = [&](float v) {
+        if (v == v) atomicAdd(&hist[(uint32_t)fminf(fmaxf(floorf((v - mn) * scale), 0.f), (float)(NBINS - 1))], 1u);
+    };
+    if (resident) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t i = i0 + j * NT;
-            v[j] = i < n ? row[i] : __builtin_nanf("");
+        for (int j = 0; j < VR; ++j) bin_add(vr[j]);
+    } else {
+        for (uint32_t i0 = tid; i0 < n; i0 += 8 * NT) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t i = i0 + j * NT;
+                v[j] = i < n ? row[i] : __builtin_nanf("");
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bin_add(v[j]);
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (v[j] == v[j])
-                atomicAdd(&hist[(uint32_t)fminf(fmaxf(floorf((v[j] - mn) * scale), 0.f), (float)(NBINS - 1))], 1u);
     }
     __syncthreads();
     find_boundary<NT>(hist, rs.q0, scan, &bo);
