@@ -5,12 +5,17 @@ leg may import this package.  The product library never loads it and shares
 no code with it; see ``oracle.c`` for the definitions it implements:
 
 * the lightning-indexer score of LiteTopK Sec. 2.1 Eq. (1), summed in double
-  over every causally valid key (no blocking, no sampling), and
+  over every causally valid key (no blocking, no sampling), with lengths
+  clamped to [0, N];
+* with the FP8-scoring flag, the same score over queries quantized per
+  (query, head) row to e4m3fn (the FP8 indexer of LiteTopK Sec. 2.1; the
+  encoder is written from the OCP E4M3 definition), and
 * exact Top-k as a full sort by (score descending, index ascending)
   (LiteTopK Sec. 3.1 Eq. (2); Sample-Guided Exact Top-K Sec. 6.1 Eq. (30)).
 
 Pins (tests/test_oracle.py) tie it to things other than itself: exhaustive
-format decodes against torch/numpy casts, numpy matmul for the H = 1 inner
+format decodes and the e4m3fn encoder over every fp32 bit pattern against
+torch/numpy casts, numpy matmul for the H = 1 inner
 product, positive-orthant and sign-flip closed forms for ReLU, monotone rows,
 brute-force subset enumeration for selection, and the exactness invariants.
 """
@@ -36,16 +41,19 @@ def _load():
         lib.ora_decode.argtypes = [I, U32]
         lib.ora_decode.restype = D
         lib.ora_decode_array.argtypes = [I, P, P, I64]
+        lib.ora_encode_e4m3.argtypes = [ctypes.c_float]
+        lib.ora_encode_e4m3.restype = ctypes.c_uint8
+        lib.ora_encode_e4m3_array.argtypes = [P, P, I64, I]
         lib.ora_select_f64.argtypes = [P, I64, I, P, P]
         lib.ora_select_f64.restype = I
         lib.ora_select_f32.argtypes = [P, I64, I, P]
         lib.ora_select_f32.restype = I
-        lib.ora_fused_topk.argtypes = [P, I, P, I, P, P, P, I, I, U32, P, I, I, P, P, P, I]
+        lib.ora_fused_topk.argtypes = [P, I, P, I, P, P, P, I64, I, I, U32, P, I, I, P, P, P, I]
         lib.ora_fused_topk.restype = I
-        lib.ora_fused_scores_at.argtypes = [P, I, P, I, P, P, I, I, U32, P, P, I64, P]
+        lib.ora_fused_scores_at.argtypes = [P, I, P, I, P, P, I64, I, I, U32, P, P, I64, P]
         lib.ora_fused_scores_at.restype = I
-        lib.ora_fused_score_row.argtypes = [P, I, P, I, P, P, I, I, U32, I, I64, P]
-        lib.ora_fused_score_row.restype = I
+        lib.ora_fused_score_row.argtypes = [P, I, P, I, P, P, I64, I, I, U32, I, I64, P]
+        lib.ora_fused_score_row.restype = I64
         lib.ora_topk_ragged.argtypes = [P, I64, P, P, I, I, P, P, I]
         lib.ora_topk_ragged.restype = I
         _lib = lib
@@ -69,6 +77,20 @@ def decode(bits: np.ndarray, dtype: int) -> np.ndarray:
     out = np.empty(src.shape, dtype=np.float64)
     _load().ora_decode_array(dtype, _ptr(src), _ptr(out), src.size)
     return out
+
+
+def encode_e4m3(x: np.ndarray, nthreads: Optional[int] = None) -> np.ndarray:
+    """e4m3fn codes (uint8) of float32 values: nearest value, ties to even;
+    NaN (0x7F, sign kept) for NaN, inf and magnitudes that round above 448."""
+    src = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(src.shape, dtype=np.uint8)
+    _load().ora_encode_e4m3_array(_ptr(src), _ptr(out), src.size, nthreads or default_threads())
+    return out
+
+
+def valid_len(case, t: int) -> int:
+    """L_t = min(max(kv_len[t], 0), N)."""
+    return int(min(max(int(case.kv_len[t]), 0), case.N))
 
 
 def select(row: np.ndarray, k: int):
@@ -113,7 +135,7 @@ def fused_topk(case, rows: Optional[Sequence[int]] = None, nthreads: Optional[in
     val = np.empty((R, case.k), dtype=np.float64)
     n = np.empty(R, dtype=np.int32)
     rc = _load().ora_fused_topk(_ptr(Q), case.q_dtype, _ptr(K), case.k_dtype, _ptr(S), _ptr(W),
-                                _ptr(kv), case.H, case.D, case.flags, _ptr(rows), R, case.k,
+                                _ptr(kv), case.N, case.H, case.D, case.flags, _ptr(rows), R, case.k,
                                 _ptr(idx), _ptr(val), _ptr(n), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"ora_fused_topk failed: {rc}")
@@ -121,13 +143,14 @@ def fused_topk(case, rows: Optional[Sequence[int]] = None, nthreads: Optional[in
 
 
 def fused_score_row(case, t: int, L: Optional[int] = None) -> np.ndarray:
-    """The full float64 score row of query ``t`` over keys [0, L)."""
+    """The full float64 score row of query ``t`` over keys [0, L), L clamped
+    to [0, N] (default: kv_len[t])."""
     L = int(case.kv_len[t]) if L is None else int(L)
     Q, K, S, W = _fused_arrays(case)
-    out = np.empty(L, dtype=np.float64)
+    out = np.empty(max(0, min(L, case.N)), dtype=np.float64)
     rc = _load().ora_fused_score_row(_ptr(Q), case.q_dtype, _ptr(K), case.k_dtype, _ptr(S), _ptr(W),
-                                     case.H, case.D, case.flags, int(t), L, _ptr(out))
-    if rc != 0:
+                                     case.N, case.H, case.D, case.flags, int(t), L, _ptr(out))
+    if rc != out.size:
         raise RuntimeError(f"ora_fused_score_row failed: {rc}")
     return out
 
@@ -139,7 +162,7 @@ def fused_scores_at(case, t_idx, j_idx) -> np.ndarray:
     Q, K, S, W = _fused_arrays(case)
     out = np.empty(t_idx.size, dtype=np.float64)
     rc = _load().ora_fused_scores_at(_ptr(Q), case.q_dtype, _ptr(K), case.k_dtype, _ptr(S), _ptr(W),
-                                     case.H, case.D, case.flags, _ptr(t_idx), _ptr(j_idx), t_idx.size,
+                                     case.N, case.H, case.D, case.flags, _ptr(t_idx), _ptr(j_idx), t_idx.size,
                                      _ptr(out))
     if rc != 0:
         raise RuntimeError(f"ora_fused_scores_at failed: {rc}")

@@ -18,6 +18,19 @@
  *    FP8 keys are dequantised as decode(k8[j,d]) * scale[j].
  *    Arithmetic: every input is widened exactly to double; products and sums
  *    are accumulated in double, sequentially over d and then over h.
+ *    Valid lengths are clamped: L_t = min(max(kv_len[t], 0), N).
+ *
+ *  - FP8 scoring (the FP8_SCORE flag, FP8 keys only): the DSA indexer of
+ *    LiteTopK Sec. 2.1 multiplies FP8 queries with FP8 keys.  Each
+ *    (query, head) row q[t,h,:] is quantized on its own: with
+ *    a = max_d |q[t,h,d]| > 0, the code of element d is the e4m3fn value
+ *    nearest (ties to even) to q[t,h,d] * (448 / a), where 448 / a and the
+ *    product are each rounded to fp32 (the code is an integer decision, so
+ *    it is taken in the precision the kernel takes it in), and the row's
+ *    scale is s = a / 448 rounded to fp32 (a row of zeros keeps code 0 and
+ *    s = 1).  The score is then Eq. (1) over the dequantized rows,
+ *        I[t,j] = sum_h w[t,h] * s[t,h] * ReLU( code[t,h,:] . k[j,:] ),
+ *    summed in double like the plain score.
  *
  *  - Exact Top-k (LiteTopK Sec. 3.1 Eq. (2); the exactness criterion of the
  *    Sample-Guided Exact Top-K paper, Sec. 6.1 Eq. (30)): sort the valid
@@ -30,6 +43,8 @@
  *  - fp16 (IEEE-754 binary16): 1 sign, 5 exponent (bias 15), 10 fraction bits.
  *  - e4m3fn (OCP 8-bit floating point, E4M3): 1 sign, 4 exponent (bias 7),
  *    3 fraction bits, no infinities, S.1111.111 is NaN, largest finite 448.
+ *    Encoding rounds to the nearest value, ties to the even fraction; a
+ *    magnitude that rounds above 448 (i.e. above 464), inf and NaN give NaN.
  */
 #include <math.h>
 #include <pthread.h>
@@ -38,7 +53,7 @@
 #include <string.h>
 
 enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_F16 = 2, ORA_FP8_E4M3 = 3 };
-enum { ORA_FLAG_NO_RELU = 1 };
+enum { ORA_FLAG_NO_RELU = 1, ORA_FLAG_FP8_SCORE = 2 };
 
 /* Generic binary floating-point decode: sign bit, ebits exponent bits,
  * mbits fraction bits, bias; `has_inf` selects IEEE-style inf/NaN at the top
@@ -88,6 +103,64 @@ void ora_decode_array(int dtype, const void *src, double *dst, int64_t n)
     }
 }
 
+/* e4m3fn encoding of an fp32 value, from the format's value set: the
+ * magnitude is divided by the spacing of its binade (2^-9 below the smallest
+ * normal 2^-6, else 2^(e-3) for 2^e <= |x| < 2^(e+1)), which is exact in
+ * double, rounded to the nearest integer with ties to even (rint under the
+ * default rounding mode), and scaled back; the result is then written as
+ * sign, biased exponent and fraction.  Results above 448 are NaN (0x7F). */
+uint8_t ora_encode_e4m3(float x)
+{
+    const double v = (double)x;
+    const uint8_t sign = signbit(x) ? 0x80u : 0u;
+    if (isnan(v)) return (uint8_t)(sign | 0x7Fu);
+    const double a = fabs(v);
+    if (isinf(a)) return (uint8_t)(sign | 0x7Fu);
+    const double min_normal = ldexp(1.0, -6);
+    double spacing;
+    if (a < min_normal) {
+        spacing = ldexp(1.0, -9);
+    } else {
+        int e;
+        (void)frexp(a, &e);          /* a = f * 2^e, 0.5 <= f < 1 */
+        spacing = ldexp(1.0, (e - 1) - 3);
+    }
+    const double r = rint(a / spacing) * spacing;
+    if (r > 448.0) return (uint8_t)(sign | 0x7Fu);
+    if (r == 0.0) return sign;
+    if (r < min_normal) return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -9)));  /* subnormal */
+    int e;
+    const double f = frexp(r, &e);   /* r = (2 f) * 2^(e-1), 1 <= 2f < 2 */
+    const int E = (e - 1) + 7;
+    const int m = (int)((2.0 * f - 1.0) * 8.0);
+    return (uint8_t)(sign | (uint8_t)(E << 3) | (uint8_t)m);
+}
+
+typedef struct { const float *src; uint8_t *dst; int64_t n, lo, hi; } enc_job_t;
+
+static void *enc_worker(void *p)
+{
+    enc_job_t *j = (enc_job_t *)p;
+    for (int64_t i = j->lo; i < j->hi; ++i) j->dst[i] = ora_encode_e4m3(j->src[i]);
+    return NULL;
+}
+
+/* Encodes n values, split over `nthreads` threads. */
+void ora_encode_e4m3_array(const float *src, uint8_t *dst, int64_t n, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 64) nthreads = 64;
+    pthread_t th[64];
+    enc_job_t jobs[64];
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = (enc_job_t){src, dst, n, n * i / nthreads, n * (i + 1) / nthreads};
+        if (pthread_create(&th[started], NULL, enc_worker, &jobs[i]) == 0) ++started;
+        else enc_worker(&jobs[i]);
+    }
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+}
+
 /* ---- decode tables (built once from ora_decode) --------------------------- */
 static double g_lut16[3][65536];
 static double g_lut8[256];
@@ -114,19 +187,45 @@ typedef struct {
     const float *k_scale;
     const float *W;
     int H, D;
+    int64_t N;
     uint32_t flags;
 } fused_args;
 
-/* Query rows widened once: qbuf[h*D + d] = q[t,h,d]. */
-static void load_query(const fused_args *a, int t, double *qbuf)
+/* L_t = min(max(kv_len[t], 0), N). */
+static int64_t valid_len(int64_t kv, int64_t N)
 {
-    for (int h = 0; h < a->H; ++h)
+    if (kv < 0) return 0;
+    return kv > N ? N : kv;
+}
+
+/* Query rows widened once: qbuf[h*D + d] = q[t,h,d] and hfac[h] = 1; with
+ * FP8 scoring, qbuf holds the decoded e4m3fn codes of each (t,h) row and
+ * hfac[h] its fp32 scale a / 448 (see the header for the quantization). */
+static void load_query(const fused_args *a, int t, double *qbuf, double *hfac)
+{
+    for (int h = 0; h < a->H; ++h) {
         for (int d = 0; d < a->D; ++d)
             qbuf[h * a->D + d] = elem(a->Q, a->q_t, ((int64_t)t * a->H + h) * a->D + d);
+        hfac[h] = 1.0;
+        if (!(a->flags & ORA_FLAG_FP8_SCORE)) continue;
+        float amax = 0.0f;  /* the inputs are bf16/fp16/fp32 values: exact in float */
+        for (int d = 0; d < a->D; ++d) {
+            const float x = (float)fabs(qbuf[h * a->D + d]);
+            if (x > amax) amax = x;
+        }
+        const int usable = amax > 0.0f && isfinite(amax);
+        const float inv = usable ? 448.0f / amax : 0.0f;
+        for (int d = 0; d < a->D; ++d) {
+            const float y = (float)qbuf[h * a->D + d] * inv;  /* fp32 product */
+            qbuf[h * a->D + d] = ora_decode(ORA_FP8_E4M3, ora_encode_e4m3(y));
+        }
+        hfac[h] = usable ? (double)(amax / 448.0f) : 1.0;
+    }
 }
 
 /* I[t,j]: the definition, in double (sequential over d, then over h). */
-static double score_key(const fused_args *a, const double *qbuf, int t, int64_t j, double *kbuf)
+static double score_key(const fused_args *a, const double *qbuf, const double *hfac, int t, int64_t j,
+                        double *kbuf)
 {
     const int H = a->H, D = a->D;
     const double sc = (a->k_t == ORA_FP8_E4M3 && a->k_scale) ? (double)a->k_scale[j] : 1.0;
@@ -135,7 +234,7 @@ static double score_key(const fused_args *a, const double *qbuf, int t, int64_t 
     for (int h = 0; h < H; ++h) {
         double dot = 0.0;
         for (int d = 0; d < D; ++d) dot += qbuf[h * D + d] * kbuf[d];
-        const double w = (double)a->W[(int64_t)t * H + h];
+        const double w = (double)a->W[(int64_t)t * H + h] * hfac[h];
         if (a->flags & ORA_FLAG_NO_RELU) s += w * dot;
         else s += w * (dot > 0.0 ? dot : 0.0);
     }
@@ -143,10 +242,11 @@ static double score_key(const fused_args *a, const double *qbuf, int t, int64_t 
 }
 
 /* Full score row of query t over keys [0, L). */
-static void score_row(const fused_args *a, int t, int64_t L, double *out, double *qbuf, double *kbuf)
+static void score_row(const fused_args *a, int t, int64_t L, double *out, double *qbuf, double *hfac,
+                      double *kbuf)
 {
-    load_query(a, t, qbuf);
-    for (int64_t j = 0; j < L; ++j) out[j] = score_key(a, qbuf, t, j, kbuf);
+    load_query(a, t, qbuf, hfac);
+    for (int64_t j = 0; j < L; ++j) out[j] = score_key(a, qbuf, hfac, t, j, kbuf);
 }
 
 /* ---- selection: full sort by (value desc, index asc) ----------------------- */
@@ -234,20 +334,21 @@ static void *fused_worker(void *p)
     job_t *j = (job_t *)p;
     const int H = j->fa.H, D = j->fa.D;
     double *qbuf = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *hfac = (double *)malloc(sizeof(double) * (size_t)H);
     double *kbuf = (double *)malloc(sizeof(double) * (size_t)D);
     double *row = (double *)malloc(sizeof(double) * (size_t)(j->maxL > 0 ? j->maxL : 1));
     vi_t *buf = (vi_t *)malloc(sizeof(vi_t) * (size_t)(j->maxL > 0 ? j->maxL : 1));
-    if (!qbuf || !kbuf || !row || !buf) { j->status = -2; goto out; }
+    if (!qbuf || !hfac || !kbuf || !row || !buf) { j->status = -2; goto out; }
     for (int r; (r = take_row(j)) >= 0;) {
         int t = j->rows[r];
-        int64_t L = j->kv_len[t];
-        score_row(&j->fa, t, L, row, qbuf, kbuf);
+        int64_t L = valid_len(j->kv_len[t], j->fa.N);
+        score_row(&j->fa, t, L, row, qbuf, hfac, kbuf);
         for (int64_t x = 0; x < L; ++x) { buf[x].v = row[x]; buf[x].i = x; }
         j->out_n[r] = select_sorted(buf, L, j->k, j->out_idx + (int64_t)r * j->k,
                                     j->out_val ? j->out_val + (int64_t)r * j->k : NULL);
     }
 out:
-    free(qbuf); free(kbuf); free(row); free(buf);
+    free(qbuf); free(hfac); free(kbuf); free(row); free(buf);
     return NULL;
 }
 
@@ -258,9 +359,7 @@ static void *ragged_worker(void *p)
     if (!buf) { j->status = -2; return NULL; }
     for (int r; (r = take_row(j)) >= 0;) {
         int m = j->rows[r];
-        int64_t L = j->row_len[m];
-        if (L > j->pitch) L = j->pitch;
-        if (L < 0) L = 0;
+        const int64_t L = valid_len(j->row_len[m], j->pitch);
         const float *x = j->scores + (int64_t)m * j->pitch;
         for (int64_t i = 0; i < L; ++i) { buf[i].v = (double)x[i]; buf[i].i = i; }
         j->out_n[r] = select_sorted(buf, L, j->k, j->out_idx + (int64_t)r * j->k, NULL);
@@ -286,56 +385,66 @@ static int run_threads(job_t *j, void *(*fn)(void *), int nthreads)
     return j->status;
 }
 
-/* Top-k of the fused score for the listed query rows.
- * out_idx/out_val: [nrows, k]; out_n: [nrows] = min(k, kv_len[t]). */
+/* Top-k of the fused score for the listed query rows of a call with N keys.
+ * out_idx/out_val: [nrows, k]; out_n: [nrows] = min(k, L_t). */
 int ora_fused_topk(const void *Q, int q_t, const void *K, int k_t, const float *k_scale,
-                   const float *W, const int32_t *kv_len, int H, int D, uint32_t flags,
+                   const float *W, const int32_t *kv_len, int64_t N, int H, int D, uint32_t flags,
                    const int32_t *rows, int nrows, int k, int32_t *out_idx, double *out_val,
                    int32_t *out_n, int nthreads)
 {
     pthread_once(&g_lut_once, build_luts);
-    if (k <= 0 || H <= 0 || D <= 0 || nrows < 0) return -1;
+    if (k <= 0 || H <= 0 || D <= 0 || N < 0 || nrows < 0) return -1;
     job_t j;
     memset(&j, 0, sizeof j);
-    j.fa = (fused_args){Q, q_t, K, k_t, k_scale, W, H, D, flags};
+    j.fa = (fused_args){Q, q_t, K, k_t, k_scale, W, H, D, N, flags};
     j.kv_len = kv_len;
     j.rows = rows; j.nrows = nrows; j.k = k;
     j.out_idx = out_idx; j.out_val = out_val; j.out_n = out_n;
-    for (int r = 0; r < nrows; ++r)
-        if (kv_len[rows[r]] > j.maxL) j.maxL = kv_len[rows[r]];
+    for (int r = 0; r < nrows; ++r) {
+        const int64_t L = valid_len(kv_len[rows[r]], N);
+        if (L > j.maxL) j.maxL = L;
+    }
     return run_threads(&j, fused_worker, nthreads);
 }
 
-/* Score of single (query, key) pairs: out[i] = I[t[i], j[i]]. */
+/* Score of single (query, key) pairs: out[i] = I[t[i], j[i]], for keys
+ * 0 <= j[i] < N (any other key index is rejected with -1). */
 int ora_fused_scores_at(const void *Q, int q_t, const void *K, int k_t, const float *k_scale,
-                        const float *W, int H, int D, uint32_t flags, const int32_t *t_idx,
+                        const float *W, int64_t N, int H, int D, uint32_t flags, const int32_t *t_idx,
                         const int64_t *j_idx, int64_t n, double *out)
 {
     pthread_once(&g_lut_once, build_luts);
-    fused_args a = {Q, q_t, K, k_t, k_scale, W, H, D, flags};
+    for (int64_t i = 0; i < n; ++i)
+        if (j_idx[i] < 0 || j_idx[i] >= N) return -1;
+    fused_args a = {Q, q_t, K, k_t, k_scale, W, H, D, N, flags};
     double *qbuf = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *hfac = (double *)malloc(sizeof(double) * (size_t)H);
     double *kbuf = (double *)malloc(sizeof(double) * (size_t)D);
-    if (!qbuf || !kbuf) { free(qbuf); free(kbuf); return -2; }
+    if (!qbuf || !hfac || !kbuf) { free(qbuf); free(hfac); free(kbuf); return -2; }
     for (int64_t i = 0; i < n; ++i) {
-        load_query(&a, t_idx[i], qbuf);
-        out[i] = score_key(&a, qbuf, t_idx[i], j_idx[i], kbuf);
+        load_query(&a, t_idx[i], qbuf, hfac);
+        out[i] = score_key(&a, qbuf, hfac, t_idx[i], j_idx[i], kbuf);
     }
-    free(qbuf); free(kbuf);
+    free(qbuf); free(hfac); free(kbuf);
     return 0;
 }
 
-/* Full score row of query t over keys [0, L). */
-int ora_fused_score_row(const void *Q, int q_t, const void *K, int k_t, const float *k_scale,
-                        const float *W, int H, int D, uint32_t flags, int t, int64_t L, double *out)
+/* Full score row of query t over keys [0, min(max(L, 0), N)); returns the
+ * number of scores written. */
+int64_t ora_fused_score_row(const void *Q, int q_t, const void *K, int k_t, const float *k_scale,
+                            const float *W, int64_t N, int H, int D, uint32_t flags, int t, int64_t L,
+                            double *out)
 {
     pthread_once(&g_lut_once, build_luts);
-    fused_args a = {Q, q_t, K, k_t, k_scale, W, H, D, flags};
+    fused_args a = {Q, q_t, K, k_t, k_scale, W, H, D, N, flags};
+    L = valid_len(L, N);
     double *qbuf = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *hfac = (double *)malloc(sizeof(double) * (size_t)H);
     double *kbuf = (double *)malloc(sizeof(double) * (size_t)D);
-    if (!qbuf || !kbuf) { free(qbuf); free(kbuf); return -2; }
-    score_row(&a, t, L, out, qbuf, kbuf);
-    free(qbuf); free(kbuf);
-    return 0;
+    if (!qbuf || !hfac || !kbuf) { free(qbuf); free(hfac); free(kbuf); return -2; }
+    score_row(&a, t, L, out, qbuf, hfac, kbuf);
+    free(qbuf); free(hfac); free(kbuf);
+    return L;
 }
 
 /* Standalone exact Top-k of the listed rows of a [M, pitch] fp32 matrix. */

@@ -278,3 +278,128 @@ def test_special_rows():
     assert n == 10 and list(idx[:10]) == list(range(9, -1, -1)) and (idx[10:] == -1).all()
     idx, n = oracle.select(np.zeros(0, np.float32), k)
     assert n == 0 and (idx == -1).all()
+
+
+# --------------------------------------------------- length clamping pins
+def test_fused_lengths_are_clamped_to_zero_and_n():
+    """L_t = min(max(kv_len[t], 0), N): a length past N selects like N, a
+    negative one like 0 (the operator contract of the Sample-Guided Exact
+    Top-K paper, Sec. 2.1: only valid entries are read)."""
+    c = synth.gen_fused(4, 3, 16, 120, 10, q_dtype=synth.BF16, k_dtype=synth.BF16,
+                        kv_len=[120, 120 + 77, -4, 0], seed=21)
+    c.q_bits[1], c.W[1] = c.q_bits[0], c.W[0]  # rows 0 and 1 differ only in kv_len
+    idx, val, n = oracle.fused_topk(c)
+    assert list(n) == [10, 10, 0, 0]
+    assert np.array_equal(idx[0], idx[1]) and np.array_equal(val[0], val[1])
+    assert (idx[2:] == -1).all() and np.isneginf(val[2:]).all()
+    assert oracle.fused_score_row(c, 1).size == 120 and oracle.fused_score_row(c, 2).size == 0
+    assert oracle.valid_len(c, 1) == 120 and oracle.valid_len(c, 2) == 0
+    with pytest.raises(RuntimeError):
+        oracle.fused_scores_at(c, [0], [120])
+
+
+def test_ragged_lengths_are_clamped_to_zero_and_pitch():
+    c = synth.gen_ragged(3, 64, 8, lens=[64, 64, 64], seed=3)
+    c.row_len = np.array([64, 64 + 5, -2], np.int32)
+    idx, n = oracle.topk_ragged(c)
+    assert list(n) == [8, 8, 0]
+    ref, _ = oracle.select(c.scores[1, :64], 8)
+    assert list(idx[1]) == list(ref) and (idx[2] == -1).all()
+
+
+# ------------------------------------------------- e4m3fn encoder pins
+def test_encode_e4m3_every_fp32_pattern_against_torch():
+    """The encoder (written from the OCP E4M3 value set, round to nearest,
+    ties to even) against torch's float8_e4m3fn cast on all 2^32 fp32 bit
+    patterns; NaN codes are compared as NaN."""
+    import torch
+    chunk = 1 << 26
+    for c in range((1 << 32) // chunk):
+        bits = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint32)
+        x = bits.view(np.float32)
+        ours = oracle.encode_e4m3(x)
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        both_nan = ((ours & 0x7F) == 0x7F) & ((ref & 0x7F) == 0x7F)
+        bad = (ours != ref) & ~both_nan
+        assert not bad.any(), f"fp32 0x{int(bits[np.argmax(bad)]):08x}: {ours[bad][:4]} vs {ref[bad][:4]}"
+
+
+def test_encode_e4m3_landmarks():
+    # ties to even at 2^-10 (half the smallest subnormal) and at 464 (between
+    # 448 and the NaN code); 1.0625 is halfway between 1 and 1.125
+    x = np.array([2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875, 448, 464, 464.5, -0.0], np.float32)
+    assert list(oracle.encode_e4m3(x)) == [0x00, 0x02, 0x38, 0x3A, 0x7E, 0x7E, 0x7F, 0x80]
+
+
+# ---------------------------------------------------- FP8 scoring pins
+FP8_SCORE = 2
+
+
+def test_fp8_scoring_worked_example():
+    """Quantized-query scoring worked by hand (LiteTopK Sec. 2.1: FP8 indexer).
+
+    Head 0, q = [1, 0.5, -0.30078125, 0.10009765625] (bf16 values): a = 1,
+    448 / a = 448, products 448, 224, -134.75, 44.84375.  In e4m3fn the
+    spacing is 32 on [256, 512), 16 on [128, 256), 4 on [32, 64): codes
+    448, 224, -128 (134.75 / 16 = 8.42 -> 8), 44 (44.84 / 4 = 11.2 -> 11);
+    scale s0 = fp32(1 / 448).
+    Head 1, q = [-2, 0.75, 3, 0]: a = 3, 448 / 3 = 149.333336 (fp32);
+    products -298.67, 112.0000019 (-> fp32 112), 448.0000076 (-> fp32 448), 0:
+    codes -288 (298.67 / 32 = 9.33 -> 9), 112, 448, 0; s1 = fp32(3 / 448).
+    FP8 keys (scale 1): k0 = e0, k1 = e2, k2 = [1, 1, 1, 1]; W = [0.5, 0.25].
+    Head dots: k0 -> 448, -288; k1 -> -128, 448; k2 -> 588, 272."""
+    q = np.array([[[1.0, 0.5, -0.30078125, 0.10009765625], [-2.0, 0.75, 3.0, 0.0]]], np.float32)
+    kk = np.array([[1, 0, 0, 0], [0, 0, 1, 0], [1, 1, 1, 1]], np.float32)
+    c = _case(1, 2, 4, 3, 3, q=q, kk=kk, W=np.array([[0.5, 0.25]]), q_dtype=synth.BF16,
+              k_dtype=synth.FP8_E4M3, k_scale=np.ones(3, np.float32))
+    s0 = float(np.float32(1.0) / np.float32(448.0))
+    s1 = float(np.float32(3.0) / np.float32(448.0))
+    c.flags = FP8_SCORE
+    exp = np.array([0.5 * s0 * 448, 0.25 * s1 * 448, 0.5 * s0 * 588 + 0.25 * s1 * 272])
+    np.testing.assert_array_equal(oracle.fused_score_row(c, 0), exp)
+    idx, val, n = oracle.fused_topk(c)
+    assert list(idx[0]) == [2, 1, 0] and np.array_equal(val[0], exp[[2, 1, 0]])
+    # without the flag: the plain score of the unquantized queries
+    c.flags = 0
+    plain = np.array([0.5, 0.25 * 3.0, 0.5 * (1 + 0.5 - 0.30078125 + 0.10009765625) + 0.25 * 1.75])
+    np.testing.assert_allclose(oracle.fused_score_row(c, 0), plain, rtol=1e-15)
+
+
+def test_fp8_scoring_is_identity_on_representable_rows():
+    """Rows whose values are e4m3fn values times 2^-6 with a largest
+    magnitude of 7 (= 448 * 2^-6): 448 / 7 = 64 and 7 / 448 = 2^-6 exactly,
+    every product is an e4m3fn value, so the quantized score equals the plain
+    score exactly."""
+    rng = np.random.default_rng(31)
+    T, H, D, N = 3, 5, 32, 40
+    codes = oracle.decode(rng.integers(0, 256, size=(T, H, D)).astype(np.uint8), synth.FP8_E4M3)
+    codes = np.where(np.isnan(codes), 0.0, codes)
+    codes[..., 0] = 448.0 * np.sign(rng.standard_normal((T, H)))
+    q = (codes * 2.0 ** -6).astype(np.float32)
+    kk = rng.standard_normal((N, D)).astype(np.float32)
+    scale = (2.0 ** rng.integers(-3, 3, size=N)).astype(np.float32)
+    c = _case(T, H, D, N, 6, q=q, kk=kk, q_dtype=synth.BF16, k_dtype=synth.FP8_E4M3, k_scale=scale)
+    plain = _all_rows(c)
+    c.flags = FP8_SCORE
+    np.testing.assert_array_equal(_all_rows(c), plain)
+
+
+def test_fp8_scoring_within_quantization_bound():
+    """Each quantized element moves by at most 2^-4 of itself (three fraction
+    bits, round to nearest) or, below the normal range, by 2^-10 of the row's
+    scale; ReLU is 1-Lipschitz, so |I8 - I| <= sum_h w_h sum_d
+    (2^-4 |q_hd| + 2^-10 s_h) |k_d|.  The bound is met and not vacuous: the
+    error is a small fraction of the score."""
+    c = synth.gen_fused(4, 8, 64, 300, 5, q_dtype=synth.BF16, k_dtype=synth.FP8_E4M3, seed=33)
+    exact = _all_rows(c)
+    c.flags = FP8_SCORE
+    quant = _all_rows(c)
+    q = oracle.decode(c.q_bits, synth.BF16).reshape(c.T, c.H, c.D)
+    k = oracle.decode(c.k_bits, synth.FP8_E4M3).reshape(c.N, c.D) * c.k_scale[:, None]
+    for t in range(c.T):
+        s = np.abs(q[t]).max(axis=1) / 448.0
+        per_head = 2.0 ** -4 * (np.abs(q[t]) @ np.abs(k).T) + 2.0 ** -10 * s[:, None] * np.abs(k).sum(1)[None]
+        bound = (c.W[t].astype(np.float64)[:, None] * per_head).sum(0)
+        err = np.abs(quant[t] - exact[t])
+        assert (err <= bound * (1 + 1e-12)).all()
+        assert err.max() > 0 and np.median(err / np.maximum(np.abs(exact[t]), 1e-12)) < 0.05
