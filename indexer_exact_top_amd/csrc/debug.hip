@@ -53,36 +53,39 @@ itk_status itk_debug_mfma(int32_t mtype, const void *a_frags, const void *b_frag
 {
     if (!a_frags || !b_frags || !c_out) return ITK_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
     if (mtype == M_BF16)
-        hipLaunchKernelGGL(k_debug_mfma<M_BF16>, dim3(1), dim3(64), 0, s,
-                           static_cast<const u32x4_t *>(a_frags), static_cast<const u32x4_t *>(b_frags), c_out);
+        e = launch_kernel(k_debug_mfma<M_BF16>, dim3(1), dim3(64), s, static_cast<const u32x4_t *>(a_frags),
+                          static_cast<const u32x4_t *>(b_frags), c_out);
     else if (mtype == M_F16)
-        hipLaunchKernelGGL(k_debug_mfma<M_F16>, dim3(1), dim3(64), 0, s,
-                           static_cast<const u32x4_t *>(a_frags), static_cast<const u32x4_t *>(b_frags), c_out);
+        e = launch_kernel(k_debug_mfma<M_F16>, dim3(1), dim3(64), s, static_cast<const u32x4_t *>(a_frags),
+                          static_cast<const u32x4_t *>(b_frags), c_out);
     else if (mtype == M_F32)
-        hipLaunchKernelGGL(k_debug_mfma<M_F32>, dim3(1), dim3(64), 0, s,
-                           static_cast<const float *>(a_frags), static_cast<const float *>(b_frags), c_out);
+        e = launch_kernel(k_debug_mfma<M_F32>, dim3(1), dim3(64), s, static_cast<const float *>(a_frags),
+                          static_cast<const float *>(b_frags), c_out);
     else
         return ITK_ERR_INVALID_ARG;
-    return hipGetLastError() == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+    return e == hipSuccess ? ITK_OK : ITK_ERR_HIP;
 }
 
 itk_status itk_debug_fp8(const uint8_t *in, uint16_t *bf16_out, uint16_t *f16_out, int32_t n, void *stream)
 {
     if (!in || !bf16_out || !f16_out || n <= 0) return ITK_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(k_debug_fp8, dim3((n + 1023) / 1024), dim3(256), 0, static_cast<hipStream_t>(stream), in,
-                       bf16_out, f16_out, n);
-    return hipGetLastError() == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+    const hipError_t e = launch_kernel(k_debug_fp8, dim3((n + 1023) / 1024), dim3(256),
+                                       static_cast<hipStream_t>(stream), in, bf16_out, f16_out, n);
+    return e == hipSuccess ? ITK_OK : ITK_ERR_HIP;
 }
 
 itk_status itk_debug_coarse(const float *x, uint32_t *key_out, float *endpoint_out, int32_t n, void *stream)
 {
     if (!x || !key_out || !endpoint_out || n <= 0 || n > NBINS) return ITK_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(k_debug_coarse, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), x,
-                       key_out, n);
-    if (hipGetLastError() != hipSuccess) return ITK_ERR_HIP;
-    hipLaunchKernelGGL(k_debug_endpoint, dim3(n), dim3(64), 0, static_cast<hipStream_t>(stream), endpoint_out);
-    return hipGetLastError() == hipSuccess ? ITK_OK : ITK_ERR_HIP;
+    if (launch_kernel(k_debug_coarse, dim3((n + 255) / 256), dim3(256), static_cast<hipStream_t>(stream), x, key_out,
+                      n) != hipSuccess)
+        return ITK_ERR_HIP;
+    return launch_kernel(k_debug_endpoint, dim3(n), dim3(64), static_cast<hipStream_t>(stream), endpoint_out) ==
+                   hipSuccess
+               ? ITK_OK
+               : ITK_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1366,31 +1366,31 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
 template <class C>
 hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t stream)
 {
+    hipError_t e;
     {
         StageTimer st(ST_F_MINMAX, stream);
-        hipLaunchKernelGGL(k_fused_minmax<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), 0, stream, a);
+        e = launch_kernel(k_fused_minmax<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a);
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
         StageTimer st(ST_F_HIST, stream);
-        hipLaunchKernelGGL(k_fused_samplehist<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), 0, stream, a);
+        e = launch_kernel(k_fused_samplehist<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
     {
         StageTimer st(ST_F_MAIN, stream);
         if (p.kp)
-            hipLaunchKernelGGL(k_fused_main_kp<C>, dim3((unsigned)((int64_t)p.T * p.P / FUSED_WAVES)),
-                               dim3(FUSED_THREADS), 0, stream, a);
+            e = launch_kernel(k_fused_main_kp<C>, dim3((unsigned)((int64_t)p.T * p.P / FUSED_WAVES)),
+                              dim3(FUSED_THREADS), stream, a);
         else
-            hipLaunchKernelGGL(k_fused_main<C>, dim3(p.G * p.P), dim3(FUSED_THREADS), 0, stream, a);
+            e = launch_kernel(k_fused_main<C>, dim3(p.G * p.P), dim3(FUSED_THREADS), stream, a);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
     {
         StageTimer st(ST_F_SELECT, stream);
-        hipLaunchKernelGGL(k_fused_select<C>, dim3(p.T), dim3(SEL_THREADS_HR), 0, stream, a);
+        e = launch_kernel(k_fused_select<C>, dim3(p.T), dim3(SEL_THREADS_HR), stream, a);
     }
-    return hipGetLastError();
+    return e;
 }
 
 using FusedLauncher = hipError_t (*)(const FusedPlan &, const FusedArgs &, hipStream_t);

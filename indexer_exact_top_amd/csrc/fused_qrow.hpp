@@ -695,24 +695,24 @@ hipError_t launch_qrow_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t s
     hipError_t e;
     {
         StageTimer st(ST_F_MINMAX, stream);
-        hipLaunchKernelGGL(k_qrow_sample<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), 0, stream, a);
+        e = launch_kernel(k_qrow_sample<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
     {
         StageTimer st(ST_F_HIST, stream);
-        hipLaunchKernelGGL(k_qrow_gate<C>, dim3(p.T), dim3(SEL_THREADS), 0, stream, a);
+        e = launch_kernel(k_qrow_gate<C>, dim3(p.T), dim3(SEL_THREADS), stream, a);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
     {
         StageTimer st(ST_F_MAIN, stream);
-        hipLaunchKernelGGL(k_qrow_main<C>, dim3(p.G * p.P), dim3(FUSED_THREADS), 0, stream, a);
+        e = launch_kernel(k_qrow_main<C>, dim3(p.G * p.P), dim3(FUSED_THREADS), stream, a);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
     {
         StageTimer st(ST_F_SELECT, stream);
-        hipLaunchKernelGGL(k_qrow_select<C>, dim3(p.T), dim3(SEL_THREADS), 0, stream, a);
+        e = launch_kernel(k_qrow_select<C>, dim3(p.T), dim3(SEL_THREADS), stream, a);
     }
-    return hipGetLastError();
+    return e;
 }
 
 FusedLauncher find_qrow_launcher(int qt, int kt, int d, bool relu);

@@ -213,7 +213,6 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
 hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const float *k_scale, const float *W,
                         const int32_t *kv_len, int32_t *out_idx, float *out_score, void *ws, hipStream_t stream)
 {
-    (void)hipGetLastError();  // report only this call's launch errors
     char *w = static_cast<char *>(ws);
     FusedArgs a;
     a.Q = Q; a.K = K; a.k_scale = k_scale; a.W = W; a.kv_len = kv_len;

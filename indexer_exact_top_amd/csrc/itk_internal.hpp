@@ -17,6 +17,22 @@ struct Cand {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+template <class T>
+struct same_type {
+    using type = T;
+};
+
+// Launches `kernel` on `stream` and returns the status of this launch only.
+// The thread's last-error state is neither read nor cleared, so an error left
+// pending by the caller's earlier work stays pending for the caller.
+template <class... P>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                                typename same_type<P>::type... args)
+{
+    void *ptrs[] = {static_cast<void *>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream);
+}
+
 // Planner knobs (process-global, tests only).
 struct Knobs {
     int32_t sample_stride = 0;

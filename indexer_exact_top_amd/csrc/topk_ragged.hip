@@ -497,9 +497,6 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
 hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t *row_len, int32_t *out_idx,
                          void *ws, hipStream_t stream)
 {
-    // An error left by an earlier, unrelated runtime call would otherwise be
-    // reported as this launch's failure.
-    (void)hipGetLastError();
     char *w = static_cast<char *>(ws);
     RaggedArgs a;
     a.scores = scores;
@@ -517,22 +514,22 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
     a.view_blocks = p.view_blocks; a.force = p.force;
     a.rho = p.rho; a.rho1 = p.rho1;
     const bool vec = (p.pitch % 4 == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0);
+    hipError_t e;
     {
         StageTimer st(ST_RAG_SCAN, stream);
-        if (vec) hipLaunchKernelGGL(k_ragged_scan<true>, dim3(p.M * p.P), dim3(RAG_THREADS), 0, stream, a);
-        else hipLaunchKernelGGL(k_ragged_scan<false>, dim3(p.M * p.P), dim3(RAG_THREADS), 0, stream, a);
+        e = vec ? launch_kernel(k_ragged_scan<true>, dim3(p.M * p.P), dim3(RAG_THREADS), stream, a)
+                : launch_kernel(k_ragged_scan<false>, dim3(p.M * p.P), dim3(RAG_THREADS), stream, a);
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
         StageTimer st(ST_RAG_FINISH, stream);
         if (p.M >= FIN_MANY_ROWS)
-            hipLaunchKernelGGL(k_ragged_finish<FIN_THREADS_MANY>, dim3(p.M), dim3(FIN_THREADS_MANY), 0, stream, a,
-                               vec ? 1 : 0);
+            e = launch_kernel(k_ragged_finish<FIN_THREADS_MANY>, dim3(p.M), dim3(FIN_THREADS_MANY), stream, a,
+                              vec ? 1 : 0);
         else
-            hipLaunchKernelGGL(k_ragged_finish<FIN_THREADS>, dim3(p.M), dim3(FIN_THREADS), 0, stream, a, vec ? 1 : 0);
+            e = launch_kernel(k_ragged_finish<FIN_THREADS>, dim3(p.M), dim3(FIN_THREADS), stream, a, vec ? 1 : 0);
     }
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace itk

@@ -35,7 +35,7 @@ FP8_E4M3_MAX = 448.0
 
 __all__ = [
     "F32", "BF16", "F16", "FP8_E4M3", "FLAG_NO_RELU", "FusedCase", "RaggedCase",
-    "gen_fused", "gen_ragged", "fused_config", "ragged_config", "csa_chunk", "CONFIGS",
+    "gen_fused", "gen_fused_exact", "gen_ragged", "fused_config", "ragged_config", "csa_chunk", "CONFIGS",
     "encode", "decode_reference_free",
 ]
 
@@ -66,7 +66,8 @@ class FusedCase:
 
     @property
     def sum_len(self) -> int:
-        return int(self.kv_len.astype(np.int64).sum())
+        """Valid (query, key) pairs: lengths clamped to [0, N]."""
+        return int(np.clip(self.kv_len.astype(np.int64), 0, self.N).sum())
 
     def flops(self) -> float:
         """Algorithmic multiply-add work of the contraction: 2*H*D per valid key."""
@@ -85,7 +86,8 @@ class RaggedCase:
 
     @property
     def sum_len(self) -> int:
-        return int(self.row_len.astype(np.int64).sum())
+        """Valid scores: lengths clamped to [0, pitch]."""
+        return int(np.clip(self.row_len.astype(np.int64), 0, self.pitch).sum())
 
 
 def _rng(seed: int) -> np.random.Generator:
@@ -170,6 +172,46 @@ def gen_fused(T, H, D, N, k, *, q_dtype=BF16, k_dtype=BF16, kv_len=None,
                      W=W, kv_len=kvl, flags=FLAG_NO_RELU if no_relu else 0)
 
 
+def gen_fused_exact(T, H, D, N, k, *, q_dtype=BF16, k_dtype=BF16, kv_len=None, seed=0,
+                    no_relu=False, fp8_score=False, name="fused_exact") -> FusedCase:
+    """A fused case whose scores are exact in fp32 whatever the summation order.
+
+    Q and K entries are integers in [-4, 4] (exact in every input format,
+    e4m3fn included), head weights are 1, 1/2 or 1/4 (signed when
+    ``no_relu``), and FP8 keys get per-key scales 1/2, 1 or 2.  A head's dot
+    product is then an integer of magnitude <= 16 D, and every partial sum
+    of weighted heads is a multiple of 2^-3 below 2^19, so every fp32
+    intermediate is exact and the scores, their ties and the Top-k are those
+    of the exact definition.  With ``fp8_score`` the query entries are
+    integers in [-7, 7] and every (query, head) row holds a +-7, so its
+    quantization scale max|q| / 448 is 2^-6 and the quantized row is
+    64 q (an e4m3fn value) exactly.  Small integers make ties frequent."""
+    rng = _rng(seed)
+    qmax = 7 if fp8_score else 4
+    q = rng.integers(-qmax, qmax + 1, size=(T, H, D)).astype(np.float32)
+    if fp8_score:
+        pos = rng.integers(0, D, size=(T, H))
+        sgn = np.where(rng.random((T, H)) < 0.5, -7.0, 7.0).astype(np.float32)
+        np.put_along_axis(q, pos[..., None], sgn[..., None], axis=2)
+    kf = rng.integers(-4, 5, size=(N, D)).astype(np.float32)
+    W = (2.0 ** -rng.integers(0, 3, size=(T, H))).astype(np.float32)
+    if no_relu:
+        W *= np.where(rng.random((T, H)) < 0.5, -1.0, 1.0).astype(np.float32)
+    if kv_len is None:
+        kvl = np.full(T, N, dtype=np.int32)
+    elif np.isscalar(kv_len):
+        kvl = np.full(T, int(kv_len), dtype=np.int32)
+    else:
+        kvl = np.asarray(kv_len, dtype=np.int32)
+    k_scale = None
+    if k_dtype == FP8_E4M3:
+        k_scale = (2.0 ** rng.integers(-1, 2, size=N)).astype(np.float32)
+    flags = (FLAG_NO_RELU if no_relu else 0) | (2 if fp8_score else 0)
+    return FusedCase(name=name, T=T, H=H, D=D, N=N, k=k, q_dtype=q_dtype, k_dtype=k_dtype,
+                     q_bits=encode(q, q_dtype), k_bits=encode(kf, k_dtype), k_scale=k_scale,
+                     W=W, kv_len=kvl, flags=flags)
+
+
 # Ragged row families.  "config2" is the headline recipe: N(0,1) values, each
 # valid entry replaced with probability 0.001 by N(4,1) (long tail), then
 # floor(0.01*L) distinct target positions copy the value of a uniformly drawn
@@ -233,7 +275,7 @@ def gen_ragged(M, pitch, k, *, lens=None, seed=0, family="config2", name=None) -
     scores = np.full((M, pitch), -np.inf, dtype=np.float32)
     fams = [family] * M if isinstance(family, str) else list(family)
     for r in range(M):
-        L = int(lens[r])
+        L = min(max(int(lens[r]), 0), pitch)  # a length outside [0, pitch] fills the clamped part
         if L:
             scores[r, :L] = _ragged_row(rng, L, k, fams[r], r)
     return RaggedCase(name=name or f"ragged_{family if isinstance(family, str) else 'mix'}",

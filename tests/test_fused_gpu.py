@@ -1,10 +1,12 @@
-"""indexer_topk_fused on the GPU against the CPU oracle."""
+"""indexer_topk_fused on the GPU against the CPU oracle (tests/parity.py:
+tolerance, derived fp32 bound, both directions of the k-th-score check,
+mean recall >= 0.99)."""
 import numpy as np
 import pytest
 import torch
 
 import synth
-from parity import check_fp8_score_rows, check_fused_rows
+from parity import check_fused_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +36,7 @@ def _run(itk, case, routes=False):
 def test_config1_all_rows(itk):
     case = synth.fused_config(1)
     idx, sc, routes = _run(itk, case, routes=True)
-    rec = check_fused_rows(case, range(case.T), idx, sc, min_recall=0.99)
+    rec = check_fused_rows(case, range(case.T), idx, sc)
     print(f"config1 recall mean {rec.mean():.4f} min {rec.min():.4f}; routes", np.bincount(routes).tolist())
 
 
@@ -46,19 +48,21 @@ def test_config1_all_rows(itk):
     (synth.BF16, synth.BF16, 1, 64), (synth.F16, synth.FP8_E4M3, 1, 128), (synth.BF16, synth.FP8_E4M3, 1, 256),
 ])
 def test_dtype_shapes(itk, qt, kt, H, D):
+    # lengths include 0, 1, a partial tile, k - 1, k, k + 1, N, and two
+    # outside [0, N] (clamped to N and to 0)
     T, N, k = 19, 9000, 300
-    kv = np.array([9000, 8999, 8000, 301, 300, 299, 1, 0, 64, 65, 4500] + [9000 - 37 * i for i in range(8)],
-                  dtype=np.int32)
+    kv = np.array([9000, 8999, 8000, 301, 300, 299, 1, 0, 64, 65, 4500, 9000 + 4321, -17] +
+                  [9000 - 37 * i for i in range(6)], dtype=np.int32)
     case = synth.gen_fused(T, H, D, N, k, q_dtype=qt, k_dtype=kt, kv_len=kv, seed=H * 7 + D)
     idx, sc, _ = _run(itk, case)
-    check_fused_rows(case, range(T), idx, sc, min_recall=0.95)
+    check_fused_rows(case, range(T), idx, sc)
 
 
 def test_inner_product_single_head(itk):
     case = synth.gen_fused(12, 1, 256, 20000, 500, q_dtype=synth.F16, k_dtype=synth.F16, no_relu=True,
                            unit_norm=True, seed=5)
     idx, sc, _ = _run(itk, case)
-    check_fused_rows(case, range(case.T), idx, sc, min_recall=0.95)
+    check_fused_rows(case, range(case.T), idx, sc)
 
 
 def test_relu_zero_rows_recover_exactly(itk):
@@ -92,27 +96,26 @@ def test_routes_and_plans_give_identical_sets(itk, knobs):
     itk.set_plan_opts(**knobs)
     got, gsc, routes = _run(itk, case, routes=True)
     print(knobs, "routes", np.bincount(routes).tolist())
-    check_fused_rows(case, range(case.T), got, gsc, min_recall=0.95)
+    check_fused_rows(case, range(case.T), got, gsc)
     # the kernel's own fp32 scores are route-independent, so the sets match exactly
     assert np.array_equal(np.sort(base, axis=1), np.sort(got, axis=1))
 
 
-def test_config3_sampled_rows(itk):
+def test_config3_first_queries(itk):
     case = synth.fused_config(3, T=64)
     idx, sc, routes = _run(itk, case, routes=True)
-    rows = [0, 17, 40, 63]
-    rec = check_fused_rows(case, rows, idx, sc, min_recall=0.99)
-    print(f"config3 (T=64) recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
+    rec = check_fused_rows(case, range(case.T), idx, sc)
+    print(f"config3 (T=64) recall mean {rec.mean():.4f} min {rec.min():.4f} routes {np.bincount(routes).tolist()}")
 
 
-@pytest.mark.parametrize("T,rows", [(16, [0, 9]), (1, [0])])
-def test_config4_sampled_rows(itk, T, rows):
+@pytest.mark.parametrize("T", [16, 1])
+def test_config4_few_queries(itk, T):
     """The 1M-key FP8 workload with 16 queries, and with one (a decoding
     step: all 256 workgroups come from key splits)."""
     case = synth.fused_config(4, T=T)
     idx, sc, routes = _run(itk, case, routes=True)
-    rec = check_fused_rows(case, rows, idx, sc, min_recall=0.95)
-    print(f"config4 (T={T}) recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
+    rec = check_fused_rows(case, range(T), idx, sc)
+    print(f"config4 (T={T}) recall mean {rec.mean():.4f} routes {np.bincount(routes).tolist()}")
 
 
 @pytest.mark.parametrize("knobs", [dict(force_route=1), dict(capacity=1024, rho=50.0), dict(splits=8),
@@ -129,26 +132,37 @@ def test_single_head_routes_and_plans_give_identical_sets(itk, knobs, qt, relu):
     itk.set_plan_opts(**knobs)
     got, gsc, routes = _run(itk, case, routes=True)
     print(knobs, "routes", np.bincount(routes).tolist())
-    check_fused_rows(case, [0, 1, 2, 3, 4, 5, 300, 511, 512, 599], got, gsc, min_recall=0.95)
+    check_fused_rows(case, range(T), got, gsc)
     assert np.array_equal(np.sort(base, axis=1), np.sort(got, axis=1))
 
 
 # Full-size workloads in the launch configuration the benchmark times
-# (default plan); the oracle checks sampled rows one by one.
-@pytest.mark.parametrize("cfg,rows,min_recall", [(3, [0, 1023, 2047], 0.99), (4, [0, 127], 0.95),
-                                                 (5, [0, 511, 1023], 0.99)])
-def test_full_size_sampled_rows(itk, cfg, rows, min_recall):
-    case = synth.fused_config(cfg)
-    idx, sc, routes = _run(itk, case, routes=True)
-    rec = check_fused_rows(case, rows, idx, sc, min_recall=min_recall)
-    # invariants on every row: |out| = min(k, L), distinct, in range
-    need = np.minimum(case.k, case.kv_len)
-    for t in range(case.T):
-        sel = idx[t, :need[t]]
-        assert (idx[t, need[t]:] == -1).all()
-        assert ((sel >= 0) & (sel < case.kv_len[t])).all()
-        assert np.unique(sel).size == need[t]
-    print(f"config{cfg} full size: recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
+# (default plan), every row checked against the oracle.  The GPU result of a
+# workload is computed once and shared by the tests that check its rows.
+_FULL = {}
+
+
+def _full_result(itk, cfg, fp8_score=False):
+    key = (cfg, fp8_score)
+    if key not in _FULL:
+        _FULL.clear()  # one workload's inputs on the host at a time
+        case = synth.fused_config(cfg)
+        if fp8_score:
+            case.flags |= itk.FLAG_FP8_SCORE
+        idx, sc, routes = _run(itk, case, routes=True)
+        _FULL[key] = (case, idx, sc, routes)
+    return _FULL[key]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,fp8_score,part,parts", [(3, False, 0, 2), (3, False, 1, 2), (4, False, 0, 1),
+                                                      (4, True, 0, 1), (5, False, 0, 2), (5, False, 1, 2)])
+def test_full_size_every_row(itk, cfg, fp8_score, part, parts):
+    case, idx, sc, routes = _full_result(itk, cfg, fp8_score)
+    rows = np.array_split(np.arange(case.T), parts)[part]
+    rec = check_fused_rows(case, rows, idx, sc)
+    print(f"config{cfg}{' fp8-scoring' if fp8_score else ''} rows {rows[0]}..{rows[-1]}: recall mean "
+          f"{rec.mean():.5f} min {rec.min():.5f}; routes {np.bincount(routes).tolist()}")
 
 
 @pytest.mark.parametrize("relu", [False, True])
@@ -166,13 +180,14 @@ def test_single_head_signed_weights(itk, relu):
     case.W = W
     idx, sc, routes = _run(itk, case, routes=True)
     print("routes", np.bincount(routes).tolist())
-    check_fused_rows(case, range(case.T), idx, sc, min_recall=0.95)
+    check_fused_rows(case, range(case.T), idx, sc)
 
 
-# FP8 scoring (queries quantized per row, e4m3 x e4m3 matrix cores): the scores
-# approximate the definition, so the parity bar is the quantization bound of
-# each score (parity.fp8_score_bound) plus the invariants; recall is reported.  Every route computes the same
-# quantized scores, so forced recovery returns the same sets.
+# FP8 scoring (queries quantized per row, e4m3 x e4m3 matrix cores): the
+# oracle quantizes the queries the same way (the codes are integer decisions
+# taken in fp32 on both sides), so the results are held to the ordinary
+# fp32 bar.  Every route computes the same quantized scores, so forced
+# recovery returns the same sets.
 @pytest.mark.parametrize("qt,H,D", [(synth.BF16, 64, 128), (synth.F16, 32, 64), (synth.BF16, 20, 256),
                                     (synth.BF16, 40, 64)])
 def test_fp8_scoring(itk, qt, H, D):
@@ -180,20 +195,12 @@ def test_fp8_scoring(itk, qt, H, D):
     case = synth.gen_fused(16, H, D, 30000, 512, q_dtype=qt, k_dtype=synth.FP8_E4M3, kv_len=kv, seed=H + D)
     case.flags = itk.FLAG_FP8_SCORE
     idx, sc, routes = _run(itk, case, routes=True)
-    rec = check_fp8_score_rows(case, range(case.T), idx, sc, min_recall=0.8)
+    rec = check_fused_rows(case, range(case.T), idx, sc)
     print(f"fp8 scoring H={H} D={D}: recall mean {rec.mean():.4f} min {rec.min():.4f}; routes",
           np.bincount(routes).tolist())
     itk.set_plan_opts(force_route=1)
     got, _, _ = _run(itk, case)
     assert np.array_equal(np.sort(idx, axis=1), np.sort(got, axis=1))
-
-
-def test_fp8_scoring_config4_sampled_rows(itk):
-    case = synth.fused_config(4)
-    case.flags = itk.FLAG_FP8_SCORE
-    idx, sc, routes = _run(itk, case, routes=True)
-    rec = check_fp8_score_rows(case, [0, 64, 127], idx, sc, min_recall=0.8)
-    print(f"config4 fp8 scoring: recall {rec.tolist()} routes {np.bincount(routes).tolist()}")
 
 
 @pytest.mark.parametrize("S,chunk,start,rows", [(16384, 64, 0, range(64)), (65536, 64, 32768, [0, 31, 63]),
@@ -205,7 +212,7 @@ def test_compressed_key_chunks(itk, S, chunk, start, rows):
     later chunks select 2048 of 8K-16K keys."""
     case = synth.csa_chunk(S, chunk, start=start)
     idx, sc, routes = _run(itk, case, routes=True)
-    rec = check_fused_rows(case, list(rows), idx, sc, min_recall=0.99)
+    rec = check_fused_rows(case, list(rows), idx, sc)
     print(f"csa S={S} start={start} recall min {rec.min():.4f} routes {np.bincount(routes).tolist()}")
 
 
@@ -213,14 +220,14 @@ def test_rows_whose_kth_score_is_zero(itk):
     """fp16, three heads, D = 256: rows with fewer valid keys than k select
     every key, including keys whose heads are all cut by the ReLU (score 0)
     and keys with scores far below the row's top, so the k-th score is 0 and
-    the tolerance falls back to the row's scale (found by a randomized
-    sweep; row 22 has 1279 keys for k = 2032)."""
+    the relative tolerance gives way to the derived fp32 bound (found by a
+    randomized sweep; row 22 has 1279 keys for k = 2032)."""
     kv = [368, 9013, 50511, 48233, 24873, 50511, 50511, 24726, 28579, 19988, 50511, 18789, 25830, 19206,
           29445, 25884, 20406, 30345, 50511, 45480, 38152, 26032, 1279]
     case = synth.gen_fused(23, 3, 256, 50511, 2032, q_dtype=synth.F16, k_dtype=synth.F16,
                            kv_len=np.array(kv, np.int32), seed=116552435)
     idx, sc, _ = _run(itk, case)
-    check_fused_rows(case, range(case.T), idx, sc, min_recall=0.99)
+    check_fused_rows(case, range(case.T), idx, sc)
 
 
 @pytest.mark.parametrize("qt,kt,H,D,T", [(synth.BF16, synth.BF16, 64, 128, 1), (synth.BF16, synth.FP8_E4M3, 64, 128, 3),
@@ -237,7 +244,7 @@ def test_few_queries_key_parallel(itk, qt, kt, H, D, T):
     kv[0] = N
     case = synth.gen_fused(T, H, D, N, 1024, q_dtype=qt, k_dtype=kt, kv_len=kv, seed=60 + T)
     idx, sc, routes = _run(itk, case, routes=True)
-    check_fused_rows(case, range(T), idx, sc, min_recall=0.99)
+    check_fused_rows(case, range(T), idx, sc)
     itk.set_plan_opts(force_route=1)
     try:
         ridx, rsc, _ = _run(itk, case)
@@ -253,4 +260,4 @@ def test_few_queries_fp8_scoring(itk):
                            kv_len=np.array([30001], np.int32), seed=71)
     case.flags |= itk.FLAG_FP8_SCORE
     idx, sc, _ = _run(itk, case)
-    check_fp8_score_rows(case, [0], idx, sc)
+    check_fused_rows(case, [0], idx, sc)

@@ -1,14 +1,15 @@
 """Seeded random shapes for both calls, checked against the CPU oracle:
-ragged rows of random pitch, lengths (empty and full rows), k and value
-family, bit-exact; fused calls over every supported dtype pair with random
-T, H, D, N, k, causal lengths (empty rows included), the inner-product form
-and FP8 scoring, within the tolerance (or the FP8-scoring bound)."""
+ragged rows of random pitch, lengths (empty and full rows, lengths outside
+[0, pitch]), k and value family, bit-exact; fused calls over every supported
+dtype pair with random T, H, D, N, k, causal lengths (empty rows, lengths
+outside [0, N]), the inner-product form and FP8 scoring, held to the fused
+bar of tests/parity.py (mean recall >= 0.99 per case)."""
 import numpy as np
 import pytest
 import torch
 
 import synth
-from parity import check_fp8_score_rows, check_fused_rows, check_ragged_exact
+from parity import check_fused_rows, check_ragged_exact
 
 pytestmark = pytest.mark.gpu
 
@@ -21,6 +22,8 @@ def _ragged_case(i):
     M = int(rng.integers(1, max(2, min(200, 4_000_000 // pitch))))
     lens = rng.integers(0, pitch + 1, size=M)
     lens[rng.random(M) < 0.2] = pitch
+    lens[rng.random(M) < 0.05] = pitch + int(rng.integers(1, 1000))  # clamped to the pitch
+    lens[rng.random(M) < 0.05] = -int(rng.integers(1, 1000))         # clamped to 0
     k = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 5000))]))
     fam = str(rng.choice(synth.RAGGED_FAMILIES))
     return synth.gen_ragged(M, pitch, k, lens=lens.astype(np.int32), seed=int(rng.integers(1 << 30)), family=fam)
@@ -42,6 +45,8 @@ def _fused_case(i):
     k = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 3000))]))
     kv = rng.integers(0, N + 1, size=T)
     kv[rng.random(T) < 0.3] = N
+    kv[rng.random(T) < 0.05] = N + int(rng.integers(1, 1000))  # clamped to N
+    kv[rng.random(T) < 0.05] = -int(rng.integers(1, 1000))     # clamped to 0
     case = synth.gen_fused(T, H, D, N, k, q_dtype=qt, k_dtype=kt, kv_len=kv.astype(np.int32),
                            seed=int(rng.integers(1 << 30)), no_relu=no_relu)
     return case, fp8_score
@@ -68,7 +73,4 @@ def test_random_fused(itk, i):
         assert e.status == 2 and fp8_score and case.H == 1, str(e)
         return
     torch.cuda.synchronize()
-    if fp8_score:
-        check_fp8_score_rows(case, range(case.T), idx.cpu().numpy(), sc.cpu().numpy())
-    else:
-        check_fused_rows(case, range(case.T), idx.cpu().numpy(), sc.cpu().numpy())
+    check_fused_rows(case, range(case.T), idx.cpu().numpy(), sc.cpu().numpy())

@@ -47,6 +47,18 @@ def test_families_bit_exact(itk, family):
     check_ragged_exact(case, out)
 
 
+@pytest.mark.parametrize("pitch", [65536, 10001])
+def test_lengths_outside_the_pitch_are_clamped(itk, pitch):
+    """row_len > pitch reads the whole row, a negative row_len none of it
+    (the operator contract: only valid entries are read); 10001 takes the
+    scalar path."""
+    lens = [pitch + 1, pitch + 100000, -1, -70000, pitch, 3000]
+    case = synth.gen_ragged(len(lens), pitch, 2048, lens=lens, seed=23, family="config2")
+    out, _ = _run(itk, case)
+    check_ragged_exact(case, out)
+    assert (out[2:4] == -1).all()
+
+
 def test_small_k_and_odd_pitch(itk):
     # pitch not a multiple of 4 takes the scalar path
     case = synth.gen_ragged(7, 10001, 37, lens=[10001, 9000, 36, 37, 38, 5000, 3], seed=3, family="config2")
