@@ -33,7 +33,9 @@ typedef enum {
     ITK_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad dtype */
     ITK_ERR_UNSUPPORTED = 2,   /* valid but not implemented shape or dtype pair */
     ITK_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
-    ITK_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+    ITK_ERR_HIP = 4,           /* a HIP launch or runtime call failed */
+    ITK_ERR_SCRATCH_LIMIT = 5  /* topk_ragged_noalloc: the call needs more than
+                                  ITK_RAGGED_NOALLOC_SCRATCH_BYTES of scratch */
 } itk_status;
 
 typedef enum {
@@ -89,6 +91,29 @@ size_t topk_ragged_workspace_size(int32_t M, int64_t row_pitch, int32_t k);
 itk_status topk_ragged(const float *scores, int64_t row_pitch, const int32_t *row_len,
                        int32_t M, int32_t k, int32_t *out_idx,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * topk_ragged without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same operation, arguments, kernels and results as
+ * topk_ragged; the scratch comes from a static device array of
+ * ITK_RAGGED_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs
+ * on holds until the process ends.  The call allocates nothing.
+ *
+ *   Returns ITK_ERR_SCRATCH_LIMIT, with nothing enqueued, when the shape
+ *   needs more scratch than that (topk_ragged_workspace_size(M, row_pitch, k)
+ *   gives the need; 64 rows of pitch 131072 with k = 2048 need about 30 MiB).
+ *   `stream` must belong to the current device (ITK_ERR_INVALID_ARG
+ *   otherwise); NULL is the current device's default stream.
+ *   All calls on one GPU share its array: calls that overlap in time on one
+ *   GPU (on different streams, or from different threads) race and must be
+ *   serialized by the caller.  Each call rewrites the scratch it reads, so
+ *   consecutive calls need no clearing.
+ * ------------------------------------------------------------------------ */
+#define ITK_RAGGED_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+itk_status topk_ragged_noalloc(const float *scores, int64_t row_pitch, const int32_t *row_len,
+                               int32_t M, int32_t k, int32_t *out_idx, void *stream);
 
 /* ------------------------------------------------------------------------
  * Fused lightning-indexer score + exact per-row Top-k.

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(HERE, "libitk.so")
 F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
 FLAG_NO_RELU = 1
 FLAG_FP8_SCORE = 2  # FP8 keys: quantize Q per (query, head) row and score on the FP8 matrix cores
-STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip error"}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip error", 5: "scratch limit"}
+RAGGED_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -52,6 +53,8 @@ def lib():
         L.topk_ragged_workspace_size.restype = SZ
         L.topk_ragged.argtypes = [P, I64, P, I32, I32, P, P, SZ, P]
         L.topk_ragged.restype = ctypes.c_int
+        L.topk_ragged_noalloc.argtypes = [P, I64, P, I32, I32, P, P]
+        L.topk_ragged_noalloc.restype = ctypes.c_int
         L.indexer_topk_fused_workspace_size.argtypes = [I32, I32, I32, I64, I32, ctypes.c_int, ctypes.c_int, U32]
         L.indexer_topk_fused_workspace_size.restype = SZ
         L.indexer_topk_fused.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, P, P, I32, I32, I32, I64, I32, U32,
@@ -131,6 +134,18 @@ def topk_ragged(scores, row_len, k: int, out_idx=None, workspace=None, stream=No
     st = lib().topk_ragged(_ptr(scores), pitch, _ptr(row_len), M, k, _ptr(out_idx), _ptr(workspace),
                            workspace.numel(), _stream(stream))
     _check(st, "topk_ragged")
+    return out_idx
+
+
+def topk_ragged_noalloc(scores, row_len, k: int, out_idx, stream=None):
+    """topk_ragged with the library's static scratch (no workspace, nothing
+    allocated by the call; ``out_idx`` [M, k] int32 must be given)."""
+    import torch
+    assert scores.is_cuda and scores.dtype == torch.float32 and scores.dim() == 2
+    assert scores.stride(1) == 1
+    M, pitch = scores.shape[0], scores.stride(0)
+    st = lib().topk_ragged_noalloc(_ptr(scores), pitch, _ptr(row_len), M, k, _ptr(out_idx), _stream(stream))
+    _check(st, "topk_ragged_noalloc")
     return out_idx
 
 

@@ -271,6 +271,7 @@ const char *itk_status_string(itk_status s)
     case ITK_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case ITK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case ITK_ERR_HIP: return "HIP runtime error";
+    case ITK_ERR_SCRATCH_LIMIT: return "shape needs more than the static scratch of the no-allocation call";
     default: return "unknown status";
     }
 }
