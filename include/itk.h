@@ -208,10 +208,15 @@ int32_t itk_profile_read(double *ms_out, int32_t *count_out, const char **names_
  *    accumulator values to c_out[16 l .. 16 l + 15].
  *  itk_debug_fp8: widen n e4m3fn codes to bf16 and fp16 bit patterns.
  *  itk_debug_coarse: the 11-bit coarse key of x[i] and the inclusive fp32
- *    endpoint of coarse bin i, for i < n <= 2048. */
+ *    endpoint of coarse bin i, for i < n <= 2048.
+ *  itk_debug_stream_read: reads floor(bytes / 16) 16-byte chunks of x (16-byte
+ *    aligned) with the non-temporal loads of the ragged scan over `blocks`
+ *    workgroups of 256 threads and writes each workgroup's maximum to
+ *    out[blocks]: the HBM read rate a plain streaming read reaches. */
 itk_status itk_debug_mfma(int32_t mtype, const void *a_frags, const void *b_frags, float *c_out, void *stream);
 itk_status itk_debug_fp8(const uint8_t *in, uint16_t *bf16_out, uint16_t *f16_out, int32_t n, void *stream);
 itk_status itk_debug_coarse(const float *x, uint32_t *key_out, float *endpoint_out, int32_t n, void *stream);
+itk_status itk_debug_stream_read(const void *x, uint64_t bytes, float *out, int32_t blocks, void *stream);
 
 #ifdef __cplusplus
 }

@@ -78,6 +78,8 @@ def lib():
         L.itk_debug_mfma.argtypes = [I32, P, P, P, P]
         L.itk_debug_fp8.argtypes = [P, P, P, I32, P]
         L.itk_debug_coarse.argtypes = [P, P, P, I32, P]
+        L.itk_debug_stream_read.restype = ctypes.c_int
+        L.itk_debug_stream_read.argtypes = [P, ctypes.c_uint64, P, I32, P]
         _lib = L
     return _lib
 
@@ -250,3 +252,13 @@ def debug_coarse(x):
     ep = torch.empty(n, dtype=torch.float32, device=x.device)
     _check(lib().itk_debug_coarse(_ptr(x), _ptr(key), _ptr(ep), n, _stream(None)), "itk_debug_coarse")
     return key, ep
+
+
+def debug_stream_read(x, blocks: int = 2048, out=None, stream=None):
+    """Streaming read of the bytes of tensor x (max per workgroup into out)."""
+    import torch
+    if out is None:
+        out = torch.empty(blocks, dtype=torch.float32, device=x.device)
+    _check(lib().itk_debug_stream_read(_ptr(x), x.numel() * x.element_size(), _ptr(out), blocks, _stream(stream)),
+           "itk_debug_stream_read")
+    return out

@@ -47,6 +47,31 @@ __global__ void k_debug_endpoint(float *endpoint)
 
 using namespace itk;
 
+// Streaming read of n16 16-byte chunks with the loads of the ragged scan
+// (non-temporal, eight in flight per thread): a max-reduction whose only
+// output is one word per workgroup, so the kernel's time is the read.
+__global__ __launch_bounds__(256) void k_debug_stream_read(const f32x4_t *x, uint64_t n16, float *out)
+{
+    constexpr int U = 8;
+    const uint64_t stride = (uint64_t)gridDim.x * 256u;
+    float m = -__builtin_inff();
+    for (uint64_t base = (uint64_t)blockIdx.x * 256u + threadIdx.x; base < n16; base += stride * U) {
+        f32x4_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t i = base + (uint64_t)u * stride;
+            v[u] = i < n16 ? __builtin_nontemporal_load(x + i) : f32x4_t{m, m, m, m};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) m = fmaxf(m, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+    }
+    m = wave_max(m);
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
 extern "C" {
 
 itk_status itk_debug_mfma(int32_t mtype, const void *a_frags, const void *b_frags, float *c_out, void *stream)
@@ -84,6 +109,15 @@ itk_status itk_debug_coarse(const float *x, uint32_t *key_out, float *endpoint_o
         return ITK_ERR_HIP;
     return launch_kernel(k_debug_endpoint, dim3(n), dim3(64), static_cast<hipStream_t>(stream), endpoint_out) ==
                    hipSuccess
+               ? ITK_OK
+               : ITK_ERR_HIP;
+}
+
+itk_status itk_debug_stream_read(const void *x, uint64_t bytes, float *out, int32_t blocks, void *stream)
+{
+    if (!x || !out || bytes < 16 || blocks <= 0 || (reinterpret_cast<uintptr_t>(x) & 15u)) return ITK_ERR_INVALID_ARG;
+    return launch_kernel(k_debug_stream_read, dim3(blocks), dim3(256), static_cast<hipStream_t>(stream),
+                         static_cast<const f32x4_t *>(x), (uint64_t)(bytes / 16), out) == hipSuccess
                ? ITK_OK
                : ITK_ERR_HIP;
 }
