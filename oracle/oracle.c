@@ -422,7 +422,7 @@ int ora_fused_scores_at(const void *Q, int q_t, const void *K, int k_t, const fl
     double *kbuf = (double *)malloc(sizeof(double) * (size_t)D);
     if (!qbuf || !hfac || !kbuf) { free(qbuf); free(hfac); free(kbuf); return -2; }
     for (int64_t i = 0; i < n; ++i) {
-        load_query(&a, t_idx[i], qbuf, hfac);
+        if (i == 0 || t_idx[i] != t_idx[i - 1]) load_query(&a, t_idx[i], qbuf, hfac);
         out[i] = score_key(&a, qbuf, hfac, t_idx[i], j_idx[i], kbuf);
     }
     free(qbuf); free(hfac); free(kbuf);
