@@ -181,6 +181,11 @@ typedef struct {
     int32_t force_route;    /* 0 auto; 1 exact route for every row (ragged:
                                no sample; fused: re-scoring recovery);
                                2 ragged: force the band pass */
+    int32_t ragged_route;   /* ragged mapping: 0 auto (by shape), 1 segments
+                               (view + scan per segment, finish per row),
+                               2 row-local (one workgroup per row); row-local
+                               is taken only for rows of at most 262144 scores
+                               and rho1 * k <= 4096 */
 } itk_plan_opts;
 
 /* NULL restores the defaults. */

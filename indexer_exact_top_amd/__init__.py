@@ -34,7 +34,8 @@ class ITKError(RuntimeError):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("sample_stride", ctypes.c_int32), ("rho", ctypes.c_float), ("rho1", ctypes.c_float),
-                ("capacity", ctypes.c_int32), ("splits", ctypes.c_int32), ("force_route", ctypes.c_int32)]
+                ("capacity", ctypes.c_int32), ("splits", ctypes.c_int32), ("force_route", ctypes.c_int32),
+                ("ragged_route", ctypes.c_int32)]
 
 
 def lib():
@@ -201,8 +202,8 @@ def fused_tensors(case, device="cuda"):
 
 
 # ------------------------------------------------------------------ knobs
-def set_plan_opts(sample_stride=0, rho=0.0, rho1=0.0, capacity=0, splits=0, force_route=0):
-    o = PlanOpts(sample_stride, rho, rho1, capacity, splits, force_route)
+def set_plan_opts(sample_stride=0, rho=0.0, rho1=0.0, capacity=0, splits=0, force_route=0, ragged_route=0):
+    o = PlanOpts(sample_stride, rho, rho1, capacity, splits, force_route, ragged_route)
     _check(lib().itk_set_plan_opts(ctypes.byref(o)), "itk_set_plan_opts")
 
 

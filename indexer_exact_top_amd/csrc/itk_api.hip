@@ -52,8 +52,9 @@ struct ProfRec {
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
-const char *const g_stage_names[ST_COUNT] = {"ragged_scan", "ragged_finish", "fused_sample_range",
-                                             "fused_sample_hist", "fused_main", "fused_select"};
+const char *const g_stage_names[ST_COUNT] = {"ragged_scan",      "ragged_finish", "fused_sample_range",
+                                             "fused_sample_hist", "fused_main",    "fused_select",
+                                             "ragged_rowlocal"};
 }  // namespace
 
 StageTimer::StageTimer(int stage_id, hipStream_t s) : stage(-1), stream(s)
@@ -329,6 +330,7 @@ itk_status itk_set_plan_opts(const itk_plan_opts *o)
         return ITK_OK;
     }
     if (o->sample_stride < 0 || o->capacity < 0 || o->splits < 0 || o->force_route < 0 || o->force_route > 2 ||
+        o->ragged_route < 0 || o->ragged_route > 2 ||
         !(o->rho >= 0.f) || !(o->rho1 >= 0.f))
         return ITK_ERR_INVALID_ARG;
     if (o->sample_stride > 0 && o->sample_stride > 4096) return ITK_ERR_INVALID_ARG;
@@ -338,6 +340,7 @@ itk_status itk_set_plan_opts(const itk_plan_opts *o)
     k.capacity = o->capacity;
     k.splits = o->splits;
     k.force_route = o->force_route;
+    k.route_select = o->ragged_route;
     return ITK_OK;
 }
 

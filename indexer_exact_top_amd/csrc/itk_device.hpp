@@ -214,11 +214,11 @@ struct BoundaryOut {
 
 // d = max{b : sum_{b' >= b} hist[b'] >= quota}, for NQ quotas at once (one
 // pass over the histogram).  When a quota exceeds the total, d = 0 and
-// above + eq == total.  Block of NT threads; `scan` holds NT/64 words.  Ends
-// with a barrier; the results are in `out` for every thread.
+// above + eq == total.  Block of NT threads; `scan` holds NT/64 words; `out`
+// is an array of NQ results in LDS.  Ends with a barrier; the results are in
+// `out` for every thread.
 template <int NT, int NQ>
-__device__ void find_boundaries(const uint32_t *hist, const uint32_t (&quota)[NQ], uint32_t *scan,
-                                BoundaryOut *const (&out)[NQ])
+__device__ void find_boundaries(const uint32_t *hist, const uint32_t (&quota)[NQ], uint32_t *scan, BoundaryOut *out)
 {
     constexpr int PER = NBINS / NT;
     const int tid = threadIdx.x;
@@ -243,20 +243,20 @@ __device__ void find_boundaries(const uint32_t *hist, const uint32_t (&quota)[NQ
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         if (tid == 0 && total < quota[q]) {
-            out[q]->digit = 0;
-            out[q]->above = total - hist[0];
-            out[q]->eq = hist[0];
-            out[q]->total = total;
+            out[q].digit = 0;
+            out[q].above = total - hist[0];
+            out[q].eq = hist[0];
+            out[q].total = total;
         }
         if (excl < quota[q] && excl + s >= quota[q]) {
             uint32_t cum = excl;
 #pragma unroll
             for (int i = PER - 1; i >= 0; --i) {
                 if (cum + loc[i] >= quota[q]) {
-                    out[q]->digit = (uint32_t)(tid * PER + i);
-                    out[q]->above = cum;
-                    out[q]->eq = loc[i];
-                    out[q]->total = total;
+                    out[q].digit = (uint32_t)(tid * PER + i);
+                    out[q].above = cum;
+                    out[q].eq = loc[i];
+                    out[q].total = total;
                     break;
                 }
                 cum += loc[i];
@@ -270,8 +270,7 @@ template <int NT>
 __device__ void find_boundary(const uint32_t *hist, uint32_t quota, uint32_t *scan, BoundaryOut *out)
 {
     const uint32_t q[1] = {quota};
-    BoundaryOut *const o[1] = {out};
-    find_boundaries<NT, 1>(hist, q, scan, o);
+    find_boundaries<NT, 1>(hist, q, scan, out);
 }
 
 // --------------------------------------------------------- exact select
@@ -405,7 +404,7 @@ struct NoSrc {
 // is degenerate or the boundary bin is too large to gather, the radix rounds
 // run over all n items instead.
 template <int NT, class SM, class Emit>
-__device__ void select_stashed(SM &sm, uint32_t n, uint32_t need, Emit &&emit, bool range_ready = false)
+__device__ __forceinline__ void select_stashed(SM &sm, uint32_t n, uint32_t need, Emit &&emit, bool range_ready = false)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     NoSrc nosrc;

@@ -40,6 +40,7 @@ struct Knobs {
     int32_t capacity = 0;
     int32_t splits = 0;
     int32_t force_route = 0;
+    int32_t route_select = 0;  // ragged mapping: 0 auto, 1 segments, 2 row-local
 };
 Knobs &knobs();
 
@@ -67,6 +68,23 @@ constexpr int RAG_MAX_CELLS = RAG_MAX_SPLITS * RAG_WAVES; // (segment, wave) cel
 constexpr int FIN_THREADS = 1024;
 constexpr int FIN_THREADS_MANY = 512;
 constexpr int FIN_MANY_ROWS = 256;
+// Row-local route: one workgroup of RL_THREADS per row, chunks of RL_U
+// 16-byte loads per thread, for at least RAG_RL_MIN_ROWS rows of at most
+// RAG_RL_MAX_PITCH scores and secondary counts rho1 * k of at most
+// RAG_RL_MAX_CAND (the on-chip stash holds STASH_CAP).  One CU streams a row
+// at a few tens of GB/s, so the route needs enough rows to occupy the chip:
+// measured on rows of 8K-128K scores (k = 2048), 1024 rows take 92 us
+// row-local against 106 us segmented, 64 rows 39 us against 22.5 us.
+#ifndef RL_THREADS_DEF
+#define RL_THREADS_DEF 512
+#endif
+constexpr int RL_THREADS = RL_THREADS_DEF;
+#ifndef RL_U
+#define RL_U 4
+#endif
+constexpr int64_t RAG_RL_MAX_PITCH = 262144;
+constexpr int RAG_RL_MIN_ROWS = 512;
+constexpr int RAG_RL_MAX_CAND = 4096;
 
 struct RaggedPlan {
     int32_t M = 0;
@@ -79,6 +97,8 @@ struct RaggedPlan {
     int32_t view_blocks = 0; // view stride in 16-element blocks
     float rho = 1.5f, rho1 = 1.75f;
     int32_t force = 0;
+    bool rowlocal = false;   // one workgroup per row, candidates on chip
+    int32_t rlcap = 0;       // row-local: on-chip candidate capacity
     // workspace carve
     size_t off_cnt = 0, off_ep = 0, off_slices = 0, off_band = 0, bytes = 0;
 };
@@ -142,6 +162,6 @@ struct StageTimer {
     StageTimer(int stage_id, hipStream_t s);
     ~StageTimer();
 };
-enum Stage { ST_RAG_SCAN = 0, ST_RAG_FINISH, ST_F_MINMAX, ST_F_HIST, ST_F_MAIN, ST_F_SELECT, ST_COUNT };
+enum Stage { ST_RAG_SCAN = 0, ST_RAG_FINISH, ST_F_MINMAX, ST_F_HIST, ST_F_MAIN, ST_F_SELECT, ST_RAG_ROWLOCAL, ST_COUNT };
 
 }  // namespace itk

@@ -1,7 +1,27 @@
 // Standalone exact Top-k over materialized ragged fp32 rows (gfx950).
 //
 // Follows the three phases of the Sample-Guided Exact Top-K paper
-// (arXiv 2609.08450, Sec. 4), re-mapped onto CDNA4:
+// (arXiv 2609.08450, Sec. 4), re-mapped onto CDNA4, with two of the
+// execution mappings of its Sec. 5.5 chosen on the host by shape:
+//
+//  k_ragged_rowlocal  many rows (at least RAG_RL_MIN_ROWS) of at most
+//                   RAG_RL_MAX_PITCH scores, and k small enough that the
+//                   expected candidates fit on chip: one workgroup per row
+//                   does everything in one launch.  The
+//                   row's first chunks of 16-byte loads are issued, then the
+//                   block-strided view (Sec. 4.2) gives the coarse boundaries
+//                   and their inclusive fp32 endpoints (Sec. 5.2); the row
+//                   streams through registers in double-buffered chunks, and
+//                   values at or above the primary endpoint go straight into
+//                   the on-chip candidate stash (per chunk: a count per lane,
+//                   one LDS atomic per wave, then the writes).  The refinement
+//                   (Sec. 5.4) runs on the stash; an underfilled view takes a
+//                   band pass over the row, an overflowing one the exact route
+//                   (Sec. 4.3, Table 2).  No global scratch, no second
+//                   launch; the hardware dispatcher hands rows to CUs as they
+//                   free up, which balances ragged lengths.
+//
+// Longer rows (decoding against long contexts) are cut into segments:
 //
 //  k_ragged_scan    one workgroup per (row, segment).  Phase 1: every segment
 //                   rebuilds the same block-strided view of its row (Sec. 4.2
@@ -43,6 +63,7 @@ struct RaggedArgs {
     Cand *band;      // [M][bandcap]
     int64_t pitch, seg;
     int32_t M, k, P, subcap, bandcap, view_blocks, force;
+    int32_t rlcap;   // row-local route: candidates kept on chip (<= STASH_CAP)
     float rho, rho1;
 };
 
@@ -59,7 +80,7 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
 {
     __shared__ uint32_t hist[NBINS];
     __shared__ uint32_t scan_tmp[16];
-    __shared__ BoundaryOut b0, b1;
+    __shared__ BoundaryOut bq[2];  // primary, secondary boundary
     __shared__ float s_e[2];
 
     // the wave index is read into a scalar register, so that the slice
@@ -128,11 +149,10 @@ __global__ __launch_bounds__(RAG_THREADS) void k_ragged_scan(RaggedArgs a)
     const bool admit_all = (n_a < q1) || q0 == 0u || ((double)a.rho1 * a.k >= (double)L);
     if (!admit_all) {
         const uint32_t qs[2] = {q0, q1};
-        BoundaryOut *const bs[2] = {&b0, &b1};
-        find_boundaries<RAG_THREADS, 2>(hist, qs, scan_tmp, bs);
+        find_boundaries<RAG_THREADS, 2>(hist, qs, scan_tmp, bq);
     }
     if (wave < 2) {  // wave 0: primary endpoint, wave 1: secondary
-        const float e = admit_all ? -__builtin_inff() : coarse_endpoint_wave(wave == 0 ? b0.digit : b1.digit);
+        const float e = admit_all ? -__builtin_inff() : coarse_endpoint_wave(bq[wave].digit);
         if (lane == 0) s_e[wave] = e;
     }
     __syncthreads();
@@ -432,6 +452,219 @@ __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
     if (tid == 0 && a.route) a.route[r] = route;
 }
 
+
+// ------------------------------------------------------------ row-local
+// One workgroup of RL_THREADS per row (see the header).  Chunks of RL_U
+// 16-byte loads per thread are double-buffered in registers.
+template <bool VEC>
+__global__ __launch_bounds__(RL_THREADS, 4) void k_ragged_rowlocal(RaggedArgs a)
+{
+    __shared__ SelectSmem sm;
+    __shared__ BoundaryOut bq[2];  // primary, secondary boundary
+    __shared__ float s_e[2];
+    __shared__ uint32_t s_cnt;
+    constexpr int NT = RL_THREADS;
+    constexpr int U = RL_U;
+    constexpr uint32_t CHUNK = (uint32_t)NT * U * 4;  // scores per chunk
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = blockIdx.x;
+    const uint32_t L = row_length(a, r);
+    const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+    int32_t *out = a.out_idx + (size_t)r * a.k;
+    for (uint32_t i = need + tid; i < (uint32_t)a.k; i += NT) out[i] = -1;
+    if (need == 0) {
+        if (tid == 0 && a.route) a.route[r] = ROUTE_ALL;
+        return;
+    }
+    const float *row = a.scores + (size_t)r * (size_t)a.pitch;
+    const uint32_t cap = (uint32_t)a.rlcap;  // <= STASH_CAP
+
+    // Chunk c: lane-interleaved 16-byte pieces of the row's whole pieces
+    // (the last 1-3 scores of a row whose length is not a multiple of 4 are
+    // admitted on their own after the chunks).  Every lane issues its U loads
+    // whatever the chunk (pieces past the row re-read piece 0, which stays in
+    // cache; admit_chunk ignores them by index), so that the number of loads
+    // in flight is the same on every path and a chunk's data is waited for
+    // with vmcnt(U) while the next chunk's loads stay in flight.  Needs
+    // n4 > 0.  Without 16-byte alignment the same positions are read one
+    // float at a time.
+    const uint32_t n4 = L >> 2;  // whole 16-byte pieces
+    auto load_chunk = [&](uint32_t c, f32x4_t (&x)[U]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i4 = c * (CHUNK / 4) + (uint32_t)(u * NT + tid);
+            const uint32_t j4 = i4 < n4 ? i4 : 0u;
+            if (VEC) {
+                x[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(row) + j4);
+            } else {
+                const float *q = row + 4u * j4;
+                x[u] = f32x4_t{q[0], q[1], q[2], q[3]};
+            }
+        }
+    };
+    f32x4_t xa[U], xb[U];
+    const bool exact_only = a.force == 1;
+    if (!exact_only && n4) load_chunk(0, xa);
+
+    // ---- view -> coarse histogram -> endpoints (as in the segmented scan)
+    float e0 = __builtin_nanf(""), e1 = __builtin_nanf("");
+    bool admit_all = false;
+    if (!exact_only) {
+        for (int i = tid; i < NBINS; i += NT) sm.hist[i] = 0u;
+        if (tid == 0) s_cnt = 0u;
+        __syncthreads();
+        const uint32_t sb = (uint32_t)a.view_blocks;
+        const uint32_t phase = (uint32_t)r % sb;
+        const uint32_t nb_total = (L + 15u) >> 4;
+        const uint32_t nvb = nb_total > phase ? (nb_total - 1u - phase) / sb + 1u : 0u;
+        for (uint32_t v0 = 0; v0 < nvb * 16u; v0 += NT * 4u) {
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = v0 + j * NT + tid;
+                const uint32_t i = (phase + (e >> 4) * sb) * 16u + (e & 15u);
+                x[j] = (e < nvb * 16u && i < L) ? row[i] : __builtin_nanf("");
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (x[j] == x[j]) atomicAdd(&sm.hist[coarse_key(x[j])], 1u);
+        }
+        __syncthreads();
+        uint32_t n_a = 0;
+        if (nvb) {
+            const uint32_t last = (phase + (nvb - 1u) * sb) * 16u;
+            n_a = (nvb - 1u) * 16u + ((L - last) < 16u ? (L - last) : 16u);
+        }
+        const double frac = (double)n_a / (double)L;
+        const uint32_t q0 = (uint32_t)ceil((double)a.rho * a.k * frac);
+        const uint32_t q1 = (uint32_t)ceil((double)a.rho1 * a.k * frac);
+        admit_all = (n_a < q1) || q0 == 0u || ((double)a.rho1 * a.k >= (double)L);
+        if (!admit_all) {
+            const uint32_t qs[2] = {q0, q1};
+            find_boundaries<NT, 2>(sm.hist, qs, sm.scan, bq);
+        }
+        if (wave < 2) {  // wave 0: primary endpoint, wave 1: secondary
+            const float e = admit_all ? -__builtin_inff() : coarse_endpoint_wave(bq[wave].digit);
+            if (lane == 0) s_e[wave] = e;
+        }
+        __syncthreads();
+        e0 = s_e[0];
+        e1 = s_e[1];
+    }
+
+    // Appends the chunk's values in [lo_edge, hi_edge) (hi_edge NaN: no upper
+    // edge) to the stash: a count per lane, one LDS atomic per wave, then the
+    // writes (slots at or past cap are dropped; the count keeps growing).
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    auto admit_chunk = [&](uint32_t c, const f32x4_t (&x)[U], float lo_edge, float hi_edge) __attribute__((always_inline)) {
+        auto in = [&](float v) __attribute__((always_inline)) { return v >= lo_edge && !(v >= hi_edge); };
+        uint32_t n = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool valid = c * (CHUNK / 4) + (uint32_t)(u * NT + tid) < n4;
+            if (valid)
+                n += (uint32_t)in(x[u].x) + (uint32_t)in(x[u].y) + (uint32_t)in(x[u].z) + (uint32_t)in(x[u].w);
+        }
+        const uint32_t incl = wave_incl_sum(n);
+        const uint32_t total = lane_value(incl, 63);
+        if (total == 0u) return;  // wave-uniform
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&s_cnt, total);
+        uint32_t slot = lane_value(base, 0) + incl - n;
+        if (n == 0u) return;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i0 = 4u * (c * (CHUNK / 4) + (uint32_t)(u * NT + tid));
+            if (i0 >= 4u * n4) continue;  // past the row's whole pieces
+            const float v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (in(v[q])) {
+                    if (slot < cap) sm.stash[slot] = make_key(v[q], i0 + (uint32_t)q);
+                    mn = fminf(mn, v[q]);
+                    mx = fmaxf(mx, v[q]);
+                    ++slot;
+                }
+            }
+        }
+    };
+    // The row's last L % 4 scores (wave 0).
+    auto admit_rest = [&](float lo_edge, float hi_edge) __attribute__((always_inline)) {
+        const uint32_t i = 4u * n4 + (uint32_t)lane;
+        if (wave == 0 && 4u * n4 < L) {
+            const float v = i < L ? row[i] : __builtin_nanf("");
+            const bool ok = v >= lo_edge && !(v >= hi_edge);
+            const uint64_t m = __ballot(ok);
+            if (m) {
+                uint32_t base = 0;
+                if (lane == 0) base = atomicAdd(&s_cnt, (uint32_t)__popcll(m));
+                const uint32_t slot = lane_value(base, 0) + lanes_below(m);
+                if (ok) {
+                    if (slot < cap) sm.stash[slot] = make_key(v, i);
+                    mn = fminf(mn, v);
+                    mx = fmaxf(mx, v);
+                }
+            }
+        }
+    };
+    // Streams the whole row through registers (chunk 0 already in xa when
+    // `first_loaded`), admitting [lo_edge, hi_edge) of every chunk.
+    const uint32_t nchunks4 = (n4 + CHUNK / 4 - 1) / (CHUNK / 4);
+    auto stream = [&](float lo_edge, float hi_edge, bool first_loaded) __attribute__((always_inline)) {
+        if (n4) {
+            if (!first_loaded) load_chunk(0, xa);
+            for (uint32_t c = 0; c < nchunks4; c += 2) {
+                load_chunk(c + 1, xb);  // past the row: discarded re-reads
+                admit_chunk(c, xa, lo_edge, hi_edge);
+                load_chunk(c + 2, xa);
+                if (c + 1 < nchunks4) admit_chunk(c + 1, xb, lo_edge, hi_edge);
+            }
+        }
+        admit_rest(lo_edge, hi_edge);
+    };
+
+    int route = ROUTE_EXACT;
+    uint32_t n = 0;
+    if (!exact_only) {
+        stream(e0, __builtin_nanf(""), true);
+        __syncthreads();
+        const uint32_t C0 = s_cnt;
+        if (C0 <= cap && C0 >= need && a.force != 2) {
+            route = admit_all ? ROUTE_ALL : ROUTE_SAMPLE;
+            n = C0;
+        } else if (C0 <= cap) {
+            // Underfilled view: a second pass appends the values between the
+            // endpoints; the band route holds when C(tau1) reaches the quota
+            // and fits the stash.
+            stream(e1, e0, false);
+            __syncthreads();
+            const uint32_t C1 = s_cnt;
+            if (C1 >= need && C1 <= cap) {
+                route = ROUTE_BAND;
+                n = C1;
+            }
+        }
+    }
+    auto emit = [&](uint32_t slot, uint64_t K) {
+        if (slot < need) out[slot] = (int32_t)key_index(K);
+    };
+    if (route == ROUTE_EXACT) {
+        __syncthreads();
+        RowSrc src{row, L, VEC};
+        exact_select<NT>(sm, src, need, emit);
+    } else {
+        mn = wave_min(mn);
+        mx = wave_max(mx);
+        if (lane == 0) {
+            sm.vmin[wave] = mn;
+            sm.vmax[wave] = mx;
+        }
+        __syncthreads();
+        select_stashed<NT>(sm, n, need, emit, true);
+    }
+    if (tid == 0 && a.route) a.route[r] = route;
+}
+
 static int ceil_div_i(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
@@ -439,24 +672,6 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     const Knobs &kn = knobs();
     RaggedPlan p;
     p.M = M; p.pitch = pitch; p.k = k;
-    // about 512 workgroups (up to RAG_MAX_SPLITS segments per row, so that a
-    // few long rows, as in decoding, still spread over the chip), and below
-    // 1024 rows segments of at most 32768 scores (128 KB), so that long rows
-    // do not serialize on one workgroup
-    int target = ceil_div_i(512, M);
-    const int by_len = ceil_div_i(pitch > 0 ? pitch : 1, RAG_SEG_MAX);
-    // From 1024 rows on, one workgroup per row already fills the chip, and
-    // every extra segment repeats the row's view pass (measured on 1024 rows
-    // of 8K-128K scores: one segment per row 107 us, four 118 us).
-    if (M < 1024 && target < by_len) target = by_len;
-    if (target < 1) target = 1;
-    if (target > RAG_MAX_SPLITS) target = RAG_MAX_SPLITS;
-    if (kn.splits > 0) target = kn.splits;
-    int64_t seg = (pitch + target - 1) / target;
-    seg = ((seg + 1023) / 1024) * 1024;
-    if (seg < 4096) seg = 4096;
-    p.seg = seg;
-    p.P = ceil_div_i(pitch > 0 ? pitch : 1, seg);
     int s = pitch >= 262144 ? 128 : 64;
     if (kn.sample_stride > 0) s = kn.sample_stride;
     p.view_blocks = s;
@@ -471,6 +686,39 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     p.rho = kn.rho > 0.f ? kn.rho : rho_auto;
     p.rho1 = kn.rho1 > 0.f ? kn.rho1 : rho_auto * (7.f / 6.f);
     if (p.rho1 < p.rho) p.rho1 = p.rho;
+    p.force = kn.force_route;
+    p.bandcap = 2 * k > 2048 ? 2 * k : 2048;
+    // Row-local route: enough rows to occupy the chip, rows short enough for
+    // one workgroup, and a secondary count that leaves room in the on-chip
+    // stash.  Tests pick a mapping with the ragged_route knob (a segment
+    // count also selects the segmented route).
+    const bool rl_fits = pitch <= RAG_RL_MAX_PITCH && (double)p.rho1 * k <= (double)RAG_RL_MAX_CAND;
+    if (rl_fits && (kn.route_select == 2 || (kn.route_select == 0 && kn.splits == 0 && M >= RAG_RL_MIN_ROWS))) {
+        p.rowlocal = true;
+        p.rlcap = kn.capacity > 0 && kn.capacity < STASH_CAP ? kn.capacity : STASH_CAP;
+        p.P = 1;
+        p.seg = pitch;
+        p.bytes = 256;  // no scratch: the route works on chip
+        return p;
+    }
+    // Segmented route: about 512 workgroups (up to RAG_MAX_SPLITS segments
+    // per row, so that a few long rows, as in decoding, still spread over the
+    // chip), and below 1024 rows segments of at most 32768 scores (128 KB),
+    // so that long rows do not serialize on one workgroup
+    int target = ceil_div_i(512, M);
+    const int by_len = ceil_div_i(pitch > 0 ? pitch : 1, RAG_SEG_MAX);
+    // From 1024 rows on, one workgroup per row already fills the chip, and
+    // every extra segment repeats the row's view pass (measured on 1024 rows
+    // of 8K-128K scores: one segment per row 107 us, four 118 us).
+    if (M < 1024 && target < by_len) target = by_len;
+    if (target < 1) target = 1;
+    if (target > RAG_MAX_SPLITS) target = RAG_MAX_SPLITS;
+    if (kn.splits > 0) target = kn.splits;
+    int64_t seg = (pitch + target - 1) / target;
+    seg = ((seg + 1023) / 1024) * 1024;
+    if (seg < 4096) seg = 4096;
+    p.seg = seg;
+    p.P = ceil_div_i(pitch > 0 ? pitch : 1, seg);
     // Each segment can hold twice the row's expected secondary count (any
     // one segment may hold all of a row's top values); past 16 segments per
     // row the per-segment share shrinks in proportion, which bounds the
@@ -482,8 +730,6 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     if (kn.capacity > 0) segcap = kn.capacity;
     p.subcap = (segcap + RAG_WAVES - 1) / RAG_WAVES;
     p.subcap = (p.subcap + 63) & ~63;
-    p.bandcap = 2 * k > 2048 ? 2 * k : 2048;
-    p.force = kn.force_route;
     const size_t cells = (size_t)M * p.P * RAG_WAVES;
     size_t off = 0;
     p.off_cnt = off; off = align256(off + cells * 4);
@@ -512,9 +758,15 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
     a.seg = p.seg;
     a.M = p.M; a.k = p.k; a.P = p.P; a.subcap = p.subcap; a.bandcap = p.bandcap;
     a.view_blocks = p.view_blocks; a.force = p.force;
+    a.rlcap = p.rlcap;
     a.rho = p.rho; a.rho1 = p.rho1;
     const bool vec = (p.pitch % 4 == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0);
     hipError_t e;
+    if (p.rowlocal) {
+        StageTimer st(ST_RAG_ROWLOCAL, stream);
+        return vec ? launch_kernel(k_ragged_rowlocal<true>, dim3(p.M), dim3(RL_THREADS), stream, a)
+                   : launch_kernel(k_ragged_rowlocal<false>, dim3(p.M), dim3(RL_THREADS), stream, a);
+    }
     {
         StageTimer st(ST_RAG_SCAN, stream);
         e = vec ? launch_kernel(k_ragged_scan<true>, dim3(p.M * p.P), dim3(RAG_THREADS), stream, a)

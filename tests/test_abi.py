@@ -113,12 +113,16 @@ def test_materialized_baseline_arithmetic():
 
 def test_plan_opts_validation():
     lib = itk.lib()
-    bad = itk.PlanOpts(-1, 0, 0, 0, 0, 0)
+    bad = itk.PlanOpts(-1, 0, 0, 0, 0, 0, 0)
     assert lib.itk_set_plan_opts(ctypes.byref(bad)) == 1
-    bad = itk.PlanOpts(0, 0, 0, 0, 0, 3)
+    bad = itk.PlanOpts(0, 0, 0, 0, 0, 3, 0)
     assert lib.itk_set_plan_opts(ctypes.byref(bad)) == 1
-    ok = itk.PlanOpts(0, 0, 0, 512, 0, 0)
+    ok = itk.PlanOpts(0, 0, 0, 512, 0, 0, 0)
     assert lib.itk_set_plan_opts(ctypes.byref(ok)) == 0
-    small = lib.topk_ragged_workspace_size(64, 131072, 2048)
+    # rows of 2^20 scores take the segmented route, whose slices follow the capacity
+    small = lib.topk_ragged_workspace_size(8, 1 << 20, 2048)
     assert lib.itk_set_plan_opts(None) == 0
-    assert lib.topk_ragged_workspace_size(64, 131072, 2048) > small
+    assert lib.topk_ragged_workspace_size(8, 1 << 20, 2048) > small
+    # the row-local route (many rows of at most 2^18 scores) needs no scratch beyond a token
+    assert lib.topk_ragged_workspace_size(1024, 131072, 2048) <= 256
+    assert lib.itk_set_plan_opts(ctypes.byref(itk.PlanOpts(0, 0, 0, 0, 0, 0, 3))) == 1

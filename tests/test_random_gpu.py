@@ -52,11 +52,16 @@ def _fused_case(i):
     return case, fp8_score
 
 
+@pytest.mark.parametrize("route", [0, 2], ids=["auto", "rowlocal"])
 @pytest.mark.parametrize("i", range(N_CASES))
-def test_random_ragged(itk, i):
+def test_random_ragged(itk, i, route):
     case = _ragged_case(i)
-    out = itk.topk_ragged(torch.from_numpy(case.scores).cuda(), torch.from_numpy(case.row_len).cuda(), case.k)
-    torch.cuda.synchronize()
+    itk.set_plan_opts(ragged_route=route)
+    try:
+        out = itk.topk_ragged(torch.from_numpy(case.scores).cuda(), torch.from_numpy(case.row_len).cuda(), case.k)
+        torch.cuda.synchronize()
+    finally:
+        itk.reset_plan_opts()
     check_ragged_exact(case, out.cpu().numpy())
 
 

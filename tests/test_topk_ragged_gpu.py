@@ -1,4 +1,8 @@
-"""topk_ragged on the GPU: bit-exact index sets against the CPU oracle."""
+"""topk_ragged on the GPU: bit-exact index sets against the CPU oracle.
+
+Every test runs under both mappings of the selector: segments (view and scan
+per segment, finish per row) and row-local (one workgroup per row); rows
+longer than the row-local limit take the segments either way."""
 import numpy as np
 import pytest
 import torch
@@ -25,10 +29,11 @@ def _run(itk, case, routes=False):
     return out.cpu().numpy(), (rb.cpu().numpy() if routes else None)
 
 
-@pytest.fixture(autouse=True)
-def _reset(itk):
+@pytest.fixture(autouse=True, params=[1, 2], ids=["segments", "rowlocal"])
+def route(request, itk):
     itk.reset_plan_opts()
-    yield
+    itk.set_plan_opts(ragged_route=request.param)
+    yield request.param
     itk.reset_plan_opts()
 
 
@@ -67,28 +72,28 @@ def test_small_k_and_odd_pitch(itk):
 
 
 @pytest.mark.parametrize("force", [1, 2])
-def test_forced_routes_match(itk, force):
+def test_forced_routes_match(itk, force, route):
     case = synth.ragged_config(seed=808, M=16)
     base, _ = _run(itk, case)
-    itk.set_plan_opts(force_route=force)
+    itk.set_plan_opts(force_route=force, ragged_route=route)
     forced, routes = _run(itk, case, routes=True)
     check_ragged_exact(case, forced)
     assert np.array_equal(np.sort(base, axis=1), np.sort(forced, axis=1))
     assert (routes == (3 if force == 1 else 2)).all(), routes
 
 
-def test_tiny_view_underfills_then_recovers(itk):
+def test_tiny_view_underfills_then_recovers(itk, route):
     # A huge stride with a low target rank underfills the primary boundary.
     case = synth.gen_ragged(8, 131072, 2048, seed=5, family="off_view")
-    itk.set_plan_opts(sample_stride=2048, rho=1.0, rho1=1.01)
+    itk.set_plan_opts(sample_stride=2048, rho=1.0, rho1=1.01, ragged_route=route)
     out, routes = _run(itk, case, routes=True)
     check_ragged_exact(case, out)
     print("off_view routes:", routes.tolist())
 
 
-def test_capacity_overflow_goes_exact(itk):
+def test_capacity_overflow_goes_exact(itk, route):
     case = synth.gen_ragged(4, 65536, 2048, seed=6, family="all_equal")
-    itk.set_plan_opts(capacity=256)
+    itk.set_plan_opts(capacity=256, ragged_route=route)
     out, routes = _run(itk, case, routes=True)
     check_ragged_exact(case, out)
     assert (routes == 3).all()

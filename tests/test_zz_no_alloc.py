@@ -31,14 +31,23 @@ def _free_bytes():
 
 
 def test_noalloc_matches_workspace_call_twice(itk):
-    big = synth.ragged_config()                                   # 64 rows, pitch 131072, k = 2048
-    small = synth.gen_ragged(9, 20000, 100, lens=[20000, 19999, 100, 99, 1, 0, 20000 + 5, -3, 7777], seed=4)
-    ref, got = _both(itk, big)
-    assert np.array_equal(np.sort(ref, axis=1), np.sort(got, axis=1))
-    check_ragged_exact(big, got)
-    ref, got = _both(itk, small)                                  # the second call, smaller
-    assert np.array_equal(np.sort(ref, axis=1), np.sort(got, axis=1))
-    check_ragged_exact(small, got)
+    # rows longer than 2^18 scores take the segmented route, whose per-segment
+    # slices live in the static scratch: 8 rows of 2^20, then a smaller call
+    big = synth.gen_ragged(8, 1 << 20, 2048, lens=[1 << 20, (1 << 20) - 77, 500000, 2048, 2047, 0, 300001, 1 << 20],
+                           seed=41)
+    small = synth.gen_ragged(3, 300000, 700, lens=[300000, 299999, 65537], seed=42, family="ties_at_k")
+    assert itk.topk_ragged_workspace_size(big.M, big.pitch, big.k) > itk.topk_ragged_workspace_size(
+        small.M, small.pitch, small.k)
+    for case in (big, small):
+        ref, got = _both(itk, case)
+        assert np.array_equal(np.sort(ref, axis=1), np.sort(got, axis=1))
+        check_ragged_exact(case, got)
+    # shorter rows (the row-local route, no scratch), two calls in a row
+    for case in (synth.ragged_config(),
+                 synth.gen_ragged(9, 20000, 100, lens=[20000, 19999, 100, 99, 1, 0, 20000 + 5, -3, 7777], seed=4)):
+        ref, got = _both(itk, case)
+        assert np.array_equal(np.sort(ref, axis=1), np.sort(got, axis=1))
+        check_ragged_exact(case, got)
     # the call takes no device memory: free memory is unchanged over calls
     x = torch.from_numpy(small.scores).cuda()
     rl = torch.from_numpy(small.row_len).cuda()
@@ -54,9 +63,9 @@ def test_noalloc_matches_workspace_call_twice(itk):
 
 def test_noalloc_rejects_shapes_beyond_the_scratch(itk):
     lib = itk.lib()
-    need = lib.topk_ragged_workspace_size(1024, 131072, 2048)
+    need = lib.topk_ragged_workspace_size(64, 1 << 20, 2048)  # 64 rows of 2^20 scores: segmented route
     assert need > itk.RAGGED_NOALLOC_SCRATCH_BYTES
     x = torch.zeros((1, 16), dtype=torch.float32, device="cuda")
-    st = lib.topk_ragged_noalloc(ctypes.c_void_p(x.data_ptr()), 131072, ctypes.c_void_p(x.data_ptr()), 1024, 2048,
+    st = lib.topk_ragged_noalloc(ctypes.c_void_p(x.data_ptr()), 1 << 20, ctypes.c_void_p(x.data_ptr()), 64, 2048,
                                  ctypes.c_void_p(x.data_ptr()), None)
     assert st == 5 and lib.itk_status_string(5).startswith(b"shape needs more")
