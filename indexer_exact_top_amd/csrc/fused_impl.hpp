@@ -165,6 +165,8 @@ struct FusedArgs {
     uint32_t *tail;    // [T] candidates appended (may exceed cap)
     Cand *cand;        // [T][cap] (head rows) or [T][P][capS] (single head)
     float *samp;       // [T][samp_cap] scores of the sampled view (both paths)
+    uint32_t *hist_r;  // [T][NBINS] full-row histogram of rows under recovery (head rows)
+    uint32_t *rflag;   // [T] 1 when the row went through the grid-wide recovery (head rows)
     // single-head (query-column) path
     float *gate;       // [T] admission gate (score space)
     uint32_t *qcnt;    // [T][P] candidates per (query, key split); may exceed capS
@@ -818,7 +820,6 @@ __device__ __forceinline__ SampleIter sample_iter(const FusedArgs &a, int g, int
     int64_t first = t0 + ((phase - t0 % st) % st + st) % st;
     it.first_key = first * TILE_KEYS < hi ? first * TILE_KEYS : -1;
     it.ntiles = it.first_key >= 0 ? (int)((hi - it.first_key + it.stride_keys - 1) / it.stride_keys) : 0;
-    if (a.force == 1) it.ntiles = 0;
     return it;
 }
 
@@ -847,8 +848,14 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
     const bool active = t < a.T;
     const uint32_t L = active ? kv_length(a, t) : 0u;
     if (p == 0 && active) {  // per-call reset of the row's counters
-        for (int i = lane; i < NBINS; i += 64) a.hist[(size_t)t * NBINS + i] = 0u;
-        if (lane == 0) a.tail[t] = 0u;
+        for (int i = lane; i < NBINS; i += 64) {
+            a.hist[(size_t)t * NBINS + i] = 0u;
+            a.hist_r[(size_t)t * NBINS + i] = 0u;
+        }
+        if (lane == 0) {
+            a.tail[t] = 0u;
+            a.rflag[t] = 0u;
+        }
     }
     const uint32_t maxL = group_max_len(a, g);
     const SampleIter it = sample_iter(a, g, p, maxL);
@@ -974,7 +981,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int g, p;
     map_group_split(blockIdx.x, a.G, a.P, g, p);
-    if (a.force == 1) return;  // every row takes the re-scoring route
+    if (a.force == 1) return;  // every row takes the recovery route (the sample still sets its bins)
     const int t = g * FUSED_WAVES + wave;
     const bool active = t < a.T;
     const uint32_t L = active ? kv_length(a, t) : 0u;
@@ -1114,6 +1121,63 @@ struct WaveBlock {
     }
 };
 
+// One wave alone scores keys [k_lo, k_hi) of the query whose fragments are
+// in qf, 64 keys per step, and calls visit(key0, s) with lane l holding the
+// (scaled) score of key key0 + l (to be masked against k_hi): with coalesced
+// row loads into two register sets (two blocks in flight) and the wave's own
+// LDS rows in kblk_all when they fit (WaveBlock), else with B fragments loaded
+// straight from global memory (two register sets when a block's fragments
+// take at most 32 registers).  The scores are bit-identical to the staged
+// scan's (same MFMA order).
+template <class C, class Visit>
+__device__ __forceinline__ void wave_scan_range(const FusedArgs &a, const QFrags<C> &qf, char *kblk_all, int64_t k_lo,
+                                                int64_t k_hi, Visit &&visit)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr bool LDSB = WaveBlock<C>::OK;
+    constexpr bool PF = GlobalBlock<C>::BYTES <= 128;
+    GlobalBlock<C> ga, gb;
+    WaveBlock<C> wa, wbk;
+    char *wl = kblk_all + (LDSB ? wave * 32 * C::ROWP : 0);
+    const int boff = bfrag_lane_off<C>();
+    if constexpr (LDSB) {
+        wa.load(a, k_lo);
+        wbk.load(a, k_lo + 32);
+    } else {
+        ga.load(a, k_lo);
+    }
+    for (int64_t key0 = k_lo; key0 < k_hi; key0 += TILE_KEYS) {
+        float p0, p1;
+        if constexpr (LDSB) {
+            // LDS accesses of one wave complete in order, so each block's
+            // fragment reads are done before the next block's rows land
+            f32x16_t acc[C::HB];
+            wa.store(wl);
+            if (key0 + TILE_KEYS < k_hi) wa.load(a, key0 + TILE_KEYS);
+            block_mfma<C>(acc, qf, wl + boff);
+            p0 = reduce_block<C>(acc, qf.w);
+            wbk.store(wl);
+            if (key0 + TILE_KEYS + 32 < k_hi) wbk.load(a, key0 + TILE_KEYS + 32);
+            block_mfma<C>(acc, qf, wl + boff);
+            p1 = reduce_block<C>(acc, qf.w);
+        } else if constexpr (PF) {
+            gb.load(a, key0 + 32);
+            p0 = ga.score(qf);
+            if (key0 + TILE_KEYS < k_hi) ga.load(a, key0 + TILE_KEYS);
+            p1 = gb.score(qf);
+        } else {
+            p0 = ga.score(qf);
+            ga.load(a, key0 + 32);
+            p1 = ga.score(qf);
+            if (key0 + TILE_KEYS < k_hi) ga.load(a, key0 + TILE_KEYS);
+        }
+        float sc = combine_halves(p0, p1);
+        const int64_t key = key0 + lane;
+        if constexpr (C::SCALE) sc *= key < k_hi ? a.k_scale[key] : 1.f;
+        visit(key0, sc);
+    }
+}
+
 // ---------------------------------------------- main pass, few queries
 // Few-query variant of the main scan (decoding): every wave works alone on a
 // key range of one query (a.P ranges per query, a.span keys each), with the
@@ -1130,7 +1194,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main_kp(FusedArgs a)
     constexpr bool LDSB = WaveBlock<C>::OK;
     __shared__ __attribute__((aligned(16))) char kblk_all[LDSB ? FUSED_WAVES * 32 * C::ROWP : 16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    if (a.force == 1) return;  // every row takes the re-scoring route
+    if (a.force == 1) return;  // every row takes the recovery route (the sample still sets its bins)
     const int64_t gw = (int64_t)blockIdx.x * FUSED_WAVES + wave;
     const int t = (int)(gw / a.P);
     const int p = (int)(gw % a.P);
@@ -1170,50 +1234,9 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main_kp(FusedArgs a)
         slot = lane_value(slot, 0);
         if ((uint32_t)lane < n && slot + lane < cap) cand[slot + lane] = stage[lane];
     };
-    // Blocks of 32 keys: with coalesced row loads into two register sets
-    // (two blocks in flight) and the wave's own LDS rows (LDSB), else with
-    // B fragments loaded directly, two register sets when a block's
-    // fragments take at most 32 registers.
-    constexpr bool PF = GlobalBlock<C>::BYTES <= 128;
-    GlobalBlock<C> ga, gb;
-    WaveBlock<C> wa, wbk;
-    char *wl = kblk_all + (LDSB ? wave * 32 * C::ROWP : 0);
-    const int boff = bfrag_lane_off<C>();
-    if constexpr (LDSB) {
-        wa.load(a, k_lo);
-        wbk.load(a, k_lo + 32);
-    } else {
-        ga.load(a, k_lo);
-    }
-    for (int64_t key0 = k_lo; key0 < k_hi; key0 += TILE_KEYS) {
-        float p0, p1;
-        if constexpr (LDSB) {
-            // LDS accesses of one wave complete in order, so each block's
-            // fragment reads are done before the next block's rows land
-            f32x16_t acc[C::HB];
-            wa.store(wl);
-            if (key0 + TILE_KEYS < k_hi) wa.load(a, key0 + TILE_KEYS);
-            block_mfma<C>(acc, qf, wl + boff);
-            p0 = reduce_block<C>(acc, qf.w);
-            wbk.store(wl);
-            if (key0 + TILE_KEYS + 32 < k_hi) wbk.load(a, key0 + TILE_KEYS + 32);
-            block_mfma<C>(acc, qf, wl + boff);
-            p1 = reduce_block<C>(acc, qf.w);
-        } else if constexpr (PF) {
-            gb.load(a, key0 + 32);
-            p0 = ga.score(qf);
-            if (key0 + TILE_KEYS < k_hi) ga.load(a, key0 + TILE_KEYS);
-            p1 = gb.score(qf);
-        } else {
-            p0 = ga.score(qf);
-            ga.load(a, key0 + 32);
-            p1 = ga.score(qf);
-            if (key0 + TILE_KEYS < k_hi) ga.load(a, key0 + TILE_KEYS);
-        }
-        float s = combine_halves(p0, p1);
+    wave_scan_range<C>(a, qf, kblk_all, k_lo, k_hi, [&](int64_t key0, float s) {
         const int64_t key = key0 + lane;
         const bool valid = key < k_hi;
-        if constexpr (C::SCALE) s *= valid ? a.k_scale[key] : 1.f;
         const float b = fmaf(s, delta, off);
         const bool pass = valid && b >= gate_f;
         const uint64_t m = __ballot(pass);
@@ -1245,8 +1268,146 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main_kp(FusedArgs a)
                 gate_f = (float)gate_bin;
             }
         }
-    }
+    });
     if (stage_n) flush(stage_n);
+}
+
+
+// ---------------------------------------------- recovery over the grid
+// Rows whose candidates overflowed the buffer or fell short of min(k, L)
+// (every row with the forced route) are recovered by the whole grid in two
+// passes over their keys, the exact coarse recovery of the Sample-Guided
+// Exact Top-K paper (Table 2): pass 1 builds each flagged row's full-row
+// histogram over a monotone bin map, pass 2 scores the row again and
+// collects every key whose bin is at or above the row's boundary bin (the
+// bin of its min(k, L)-th score), which holds the exact Top-k.  The select
+// kernel then selects from those candidates as for any other row; only a
+// row whose boundary bin alone overflows the buffer (heavy ties, or a
+// degenerate range) falls back to re-scoring inside the select kernel.
+// Each flagged row is cut into key ranges, one per wave, so that a single
+// recovered row occupies the whole chip.  Every workgroup lists the flagged
+// rows itself, in index order, so that all agree on the work split.
+constexpr int RLIST = 1024;     // flagged rows listed per round (two per thread)
+constexpr int RSPAN_MIN = 512;  // keys per wave, at least
+
+__device__ __forceinline__ bool row_needs_recovery(const FusedArgs &a, int t)
+{
+    const uint32_t L = kv_length(a, t);
+    const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+    if (need == 0u) return false;
+    const uint32_t n = a.tail[t];
+    return a.force == 1 || n > (uint32_t)a.cap || n < need;
+}
+
+// Monotone bin map of the recovery histogram: the row's sampled equal-width
+// bins, or the top 11 bits of the ordered fp32 key when the sampled range
+// was degenerate.
+__device__ __forceinline__ uint32_t recovery_bin(float4 bp, float s)
+{
+    return bp.z == 0.f ? bin_of(fmaf(s, bp.y, bp.x)) : ordered_key(s) >> 21;
+}
+
+template <class C, int PASS>
+__global__ __launch_bounds__(FUSED_THREADS) void k_fused_recover(FusedArgs a)
+{
+    static_assert(RLIST == 2 * FUSED_THREADS, "two rows per thread in the listing");
+    __shared__ uint32_t list[RLIST];
+    __shared__ uint32_t s_wsum[FUSED_WAVES];
+    __shared__ uint32_t whist_all[PASS == 1 ? FUSED_WAVES : 1][PASS == 1 ? NBINS : 1];
+    __shared__ Cand stage_all[PASS == 2 ? FUSED_WAVES : 1][128];
+    constexpr bool LDSB = WaveBlock<C>::OK;
+    __shared__ __attribute__((aligned(16))) char kblk_all[LDSB ? FUSED_WAVES * 32 * C::ROWP : 16];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * FUSED_WAVES;
+    const int64_t gw = (int64_t)blockIdx.x * FUSED_WAVES + wave;
+    for (int t0 = 0; t0 < a.T; t0 += RLIST) {
+        // flagged rows of [t0, t0 + RLIST) in index order: pass 1 from the
+        // candidate counts, pass 2 from the flags pass 1 set
+        const int r0 = t0 + 2 * tid;
+        auto flagged = [&](int t) {
+            if (t >= a.T) return false;
+            return PASS == 1 ? row_needs_recovery(a, t) : a.rflag[t] != 0u;
+        };
+        const uint32_t f0 = flagged(r0) ? 1u : 0u, f1 = flagged(r0 + 1) ? 1u : 0u;
+        const uint32_t c = f0 + f1;
+        const uint32_t incl = wave_incl_sum(c);
+        if (lane == 63) s_wsum[wave] = incl;
+        __syncthreads();
+        uint32_t off = incl - c, F = 0;
+#pragma unroll
+        for (int w = 0; w < FUSED_WAVES; ++w) {
+            if (w < wave) off += s_wsum[w];
+            F += s_wsum[w];
+        }
+        if (f0) list[off] = (uint32_t)r0;
+        if (f1) list[off + f0] = (uint32_t)(r0 + 1);
+        __syncthreads();
+        if (F == 0u) continue;  // workgroup-uniform
+        int64_t span = ((int64_t)F * a.N + nwaves - 1) / nwaves;
+        span = (span + TILE_KEYS - 1) / TILE_KEYS * TILE_KEYS;
+        if (span < RSPAN_MIN) span = RSPAN_MIN;
+        const int64_t per_row = (a.N + span - 1) / span;
+        const int64_t items = (int64_t)F * per_row;
+        for (int64_t w = gw; w < items; w += nwaves) {
+            const int t = (int)list[w / per_row];
+            const int64_t p = w % per_row;
+            const uint32_t L = kv_length(a, t);
+            const int64_t lo = p * span;
+            const int64_t hi = lo + span < (int64_t)L ? lo + span : (int64_t)L;
+            if (PASS == 1 && p == 0 && lane == 0) {
+                a.rflag[t] = 1u;
+                a.tail[t] = 0u;  // pass 2 appends from 0 (the row stays flagged: 0 < min(k, L))
+            }
+            if (hi <= lo) continue;
+            const float4 bp = a.param[t];
+            QFrags<C> qf;
+            qf.load(a, t);
+            if constexpr (PASS == 1) {
+                uint32_t *whist = whist_all[wave];
+                for (int i = lane; i < NBINS; i += 64) whist[i] = 0u;
+                wave_scan_range<C>(a, qf, kblk_all, lo, hi, [&](int64_t key0, float sc) {
+                    if (key0 + lane < hi) atomicAdd(&whist[recovery_bin(bp, sc)], 1u);
+                });
+                uint32_t *hr = a.hist_r + (size_t)t * NBINS;
+                for (int i = lane; i < NBINS; i += 64) {
+                    const uint32_t cnt = whist[i];
+                    if (cnt) atomicAdd(&hr[i], cnt);
+                }
+            } else {
+                const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+                const int bnd = wave_top_bin(a.hist_r + (size_t)t * NBINS, need);  // >= 0: the row holds L >= need keys
+                const uint32_t B = bnd > 0 ? (uint32_t)bnd : 0u;
+                Cand *stage = stage_all[wave];
+                Cand *cand = a.cand + (size_t)t * a.cap;
+                const uint32_t cap = (uint32_t)a.cap;
+                uint32_t stage_n = 0;
+                auto flush = [&](uint32_t n) {
+                    uint32_t slot = 0;
+                    if (lane == 0) slot = atomicAdd(&a.tail[t], n);
+                    slot = lane_value(slot, 0);
+                    if ((uint32_t)lane < n && slot + lane < cap) cand[slot + lane] = stage[lane];
+                };
+                wave_scan_range<C>(a, qf, kblk_all, lo, hi, [&](int64_t key0, float sc) {
+                    const bool pass = key0 + lane < hi && recovery_bin(bp, sc) >= B;
+                    const uint64_t m = __ballot(pass);
+                    if (m) {
+                        if (pass) stage[stage_n + lanes_below(m)] = Cand{(uint32_t)(key0 + lane), sc};
+                        stage_n += (uint32_t)__popcll(m);
+                        if (stage_n >= 64u) {
+                            flush(64u);
+                            const bool mv = (uint32_t)lane < stage_n - 64u;
+                            Cand e;
+                            if (mv) e = stage[64 + lane];
+                            if (mv) stage[lane] = e;
+                            stage_n -= 64u;
+                        }
+                    }
+                });
+                if (stage_n) flush(stage_n);
+            }
+        }
+        __syncthreads();  // every wave is done with the list before the next round rewrites it
+    }
 }
 
 // ------------------------------------------- select (+ recovery) per row
@@ -1288,7 +1449,7 @@ struct RescoreSrc {
     }
 };
 
-enum { FROUTE_SAMPLE = 1, FROUTE_RECOVER = 3, FROUTE_ALL = 4 };
+enum { FROUTE_SAMPLE = 1, FROUTE_RECOVER = 3, FROUTE_ALL = 4, FROUTE_GRID_RECOVERY = 5 };
 
 template <class C>
 __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
@@ -1308,8 +1469,11 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
         if (tid == 0 && a.route) a.route[t] = FROUTE_ALL;
         return;
     }
+    // After the grid-wide recovery passes every row holds at least min(k, L)
+    // candidates; a row whose candidates still overflow the buffer is
+    // re-scored here.
     const uint32_t n = a.tail[t];
-    const bool recover = a.force == 1 || n > (uint32_t)a.cap || n < need;
+    const bool recover = n > (uint32_t)a.cap || n < need;
     auto emit = [&](uint32_t slot, uint64_t K) {
         if (slot < need) {
             oi[slot] = (int32_t)key_index(K);
@@ -1358,7 +1522,8 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
     if (tid == 0 && a.route) {
         const float4 bp = a.param[t];
         const RowSample rs = row_sample(a, t / FUSED_WAVES, L, bp.z != 0.f);
-        a.route[t] = recover ? FROUTE_RECOVER : (rs.admit_all ? FROUTE_ALL : FROUTE_SAMPLE);
+        a.route[t] = recover ? FROUTE_RECOVER
+                             : (a.rflag[t] ? FROUTE_GRID_RECOVERY : (rs.admit_all ? FROUTE_ALL : FROUTE_SAMPLE));
     }
 }
 
@@ -1384,6 +1549,12 @@ hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t 
                               dim3(FUSED_THREADS), stream, a);
         else
             e = launch_kernel(k_fused_main<C>, dim3(p.G * p.P), dim3(FUSED_THREADS), stream, a);
+    }
+    if (e != hipSuccess) return e;
+    {
+        StageTimer st(ST_F_RECOVER, stream);
+        e = launch_kernel(k_fused_recover<C, 1>, dim3(RECOVER_WGS), dim3(FUSED_THREADS), stream, a);
+        if (e == hipSuccess) e = launch_kernel(k_fused_recover<C, 2>, dim3(RECOVER_WGS), dim3(FUSED_THREADS), stream, a);
     }
     if (e != hipSuccess) return e;
     {

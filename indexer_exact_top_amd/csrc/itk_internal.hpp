@@ -124,6 +124,8 @@ constexpr int QROW_MAX_SPLITS = 256;  // single-head path: key splits per query
 // eight (182 against 145 us) are faster staged, where eight queries share
 // each staged key tile.
 constexpr int KP_MAX_T = 2;
+// Grid-wide recovery passes (head rows): workgroups of FUSED_THREADS, one per CU.
+constexpr int RECOVER_WGS = 256;
 constexpr int KP_WAVES = 2048;
 
 struct FusedPlan {
@@ -146,6 +148,7 @@ struct FusedPlan {
     int32_t capS = 0;        // single head: candidates per (query, key split)
     int64_t samp_cap = 0;    // single head: stored view scores per query
     size_t off_param = 0, off_mm = 0, off_hist = 0, off_tail = 0, off_gate = 0, off_cand = 0;
+    size_t off_hist_r = 0, off_rflag = 0;
     size_t off_samp = 0, off_qcnt = 0, bytes = 0;
 };
 itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk_dtype qt, itk_dtype kt,
@@ -162,6 +165,6 @@ struct StageTimer {
     StageTimer(int stage_id, hipStream_t s);
     ~StageTimer();
 };
-enum Stage { ST_RAG_SCAN = 0, ST_RAG_FINISH, ST_F_MINMAX, ST_F_HIST, ST_F_MAIN, ST_F_SELECT, ST_RAG_ROWLOCAL, ST_COUNT };
+enum Stage { ST_RAG_SCAN = 0, ST_RAG_FINISH, ST_F_MINMAX, ST_F_HIST, ST_F_MAIN, ST_F_SELECT, ST_RAG_ROWLOCAL, ST_F_RECOVER, ST_COUNT };
 
 }  // namespace itk
