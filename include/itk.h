@@ -194,10 +194,22 @@ itk_status itk_set_plan_opts(const itk_plan_opts *opts);
 /* Route taken per row by the last calls: when `route_out` (device, [rows]
  * int32) is non-NULL, each following call writes a route code per row:
  *   1 certified by the sample, 2 certified after the band pass,
- *   3 exact route (no usable sample, overflow, or underfill),
- *   4 all valid entries fit the candidate capacity (no gate needed).
+ *   3 exact route (no usable sample, overflow, or underfill; for fused calls
+ *     the single-workgroup re-scoring that remains when a row's boundary bin
+ *     alone overflows the buffer),
+ *   4 all valid entries fit the candidate capacity (no gate needed),
+ *   5 fused calls: recovered by the grid-wide recovery passes (overflow or
+ *     underfill of the sampled gate).
  * Pass NULL to stop. */
 itk_status itk_set_route_buffer(int32_t *route_out, int32_t rows);
+
+/* Candidates per row: when `count_out` (device, [rows] int32) is non-NULL,
+ * each following fused call writes, per query row, the number of candidates
+ * its selection started from (admitted by the gate of the main pass, or
+ * collected by the recovery passes for a recovered row; the single-head path
+ * counts every admitted key, also past the slices' capacity).  Pass NULL to
+ * stop. */
+itk_status itk_set_count_buffer(int32_t *count_out, int32_t rows);
 
 /* Per-kernel timing.  While enabled, each call records HIP events around each
  * kernel it launches; itk_profile_read sums the elapsed milliseconds per

@@ -69,6 +69,8 @@ def lib():
         L.itk_set_plan_opts.restype = ctypes.c_int
         L.itk_set_route_buffer.argtypes = [P, I32]
         L.itk_set_route_buffer.restype = ctypes.c_int
+        L.itk_set_count_buffer.argtypes = [P, I32]
+        L.itk_set_count_buffer.restype = ctypes.c_int
         L.itk_profile_enable.argtypes = [I32]
         L.itk_profile_enable.restype = ctypes.c_int
         L.itk_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32),
@@ -213,6 +215,10 @@ def reset_plan_opts():
 
 def set_route_buffer(t=None):
     _check(lib().itk_set_route_buffer(_ptr(t), 0 if t is None else t.numel()), "itk_set_route_buffer")
+
+
+def set_count_buffer(t=None):
+    _check(lib().itk_set_count_buffer(_ptr(t), 0 if t is None else t.numel()), "itk_set_count_buffer")
 
 
 def profile_enable(on: bool = True):

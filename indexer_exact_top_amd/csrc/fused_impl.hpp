@@ -159,6 +159,7 @@ struct FusedArgs {
     int32_t *out_idx;
     float *out_score;
     int32_t *route;
+    int32_t *count;    // [T] candidates the selection started from (test knob), or null
     float4 *param;     // [T] {off, delta, degenerate, 0}
     float2 *mm;        // [T][Ps] {min, max} of the sampled scores
     uint32_t *hist;    // [T][NBINS] sample histogram
@@ -1467,6 +1468,7 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
     }
     if (need == 0) {
         if (tid == 0 && a.route) a.route[t] = FROUTE_ALL;
+        if (tid == 0 && a.count) a.count[t] = 0;
         return;
     }
     // After the grid-wide recovery passes every row holds at least min(k, L)
@@ -1519,6 +1521,7 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
         RescoreSrc<C> src{&a, t, L};
         exact_select<SEL_THREADS_HR>(sm, src, need, emit);
     }
+    if (tid == 0 && a.count) a.count[t] = (int32_t)n;
     if (tid == 0 && a.route) {
         const float4 bp = a.param[t];
         const RowSample rs = row_sample(a, t / FUSED_WAVES, L, bp.z != 0.f);

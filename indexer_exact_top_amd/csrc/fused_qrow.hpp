@@ -609,6 +609,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
     }
     if (need == 0) {
         if (tid == 0 && a.route) a.route[t] = 4;
+        if (tid == 0 && a.count) a.count[t] = 0;
         return;
     }
     // slice counts -> prefix (cpre) and overflow flag: one slice per thread,
@@ -630,6 +631,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
     __syncthreads();
     const uint32_t n = cpre[ncell];
     const bool recover = a.force == 1 || s_ovf || n < need;
+    if (tid == 0 && a.count) {  // admitted candidates, past the slices' capacity included
+        uint32_t tot = 0;
+        for (int c = 0; c < ncell; ++c) tot += cnt[c];
+        a.count[t] = (int32_t)tot;
+    }
     auto emit = [&](uint32_t slot, uint64_t K) {
         if (slot < need) {
             oi[slot] = (int32_t)key_index(K);

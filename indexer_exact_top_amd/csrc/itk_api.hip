@@ -222,6 +222,7 @@ hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const 
     a.out_idx = out_idx; a.out_score = out_score;
     const RouteSink &rs = route_sink();
     a.route = (rs.ptr && rs.rows >= p.T) ? rs.ptr : nullptr;
+    a.count = (rs.count && rs.count_rows >= p.T) ? rs.count : nullptr;
     a.param = reinterpret_cast<float4 *>(w + p.off_param);
     a.mm = reinterpret_cast<float2 *>(w + p.off_mm);
     a.hist = reinterpret_cast<uint32_t *>(w + p.off_hist);
@@ -353,6 +354,14 @@ itk_status itk_set_route_buffer(int32_t *route_out, int32_t rows)
     if (route_out && rows <= 0) return ITK_ERR_INVALID_ARG;
     route_sink().ptr = route_out;
     route_sink().rows = route_out ? rows : 0;
+    return ITK_OK;
+}
+
+itk_status itk_set_count_buffer(int32_t *count_out, int32_t rows)
+{
+    if (count_out && rows <= 0) return ITK_ERR_INVALID_ARG;
+    route_sink().count = count_out;
+    route_sink().count_rows = count_out ? rows : 0;
     return ITK_OK;
 }
 

@@ -47,6 +47,8 @@ Knobs &knobs();
 struct RouteSink {
     int32_t *ptr = nullptr;
     int32_t rows = 0;
+    int32_t *count = nullptr;  // admitted candidates per row (fused calls)
+    int32_t count_rows = 0;
 };
 RouteSink &route_sink();
 

@@ -261,3 +261,36 @@ def test_few_queries_fp8_scoring(itk):
     case.flags |= itk.FLAG_FP8_SCORE
     idx, sc, _ = _run(itk, case)
     check_fused_rows(case, [0], idx, sc)
+
+
+@pytest.mark.parametrize("H,qt,kt,no_relu", [(64, synth.BF16, synth.BF16, False), (64, synth.BF16, synth.FP8_E4M3, False),
+                                             (1, synth.F16, synth.F16, True)])
+def test_candidate_counts(itk, H, qt, kt, no_relu):
+    """The per-row candidate count knob: a row certified by its sample
+    starts its selection from at least min(k, L) candidates, and a row with
+    no gate (route 4) from all of its L keys."""
+    T, N, k = 24, 40000, 512
+    kv = np.concatenate([np.full(19, N), [N - 7, 600, 512, 300, 0]]).astype(np.int32)
+    D = 256 if H == 1 else 128
+    case = synth.gen_fused(T, H, D, N, k, q_dtype=qt, k_dtype=kt, kv_len=kv, no_relu=no_relu, unit_norm=no_relu,
+                           seed=71 + H)
+    Q, K, S, W, kvt = itk.fused_tensors(case)
+    cnt = torch.full((T,), -1, dtype=torch.int32, device="cuda")
+    rb = torch.zeros(T, dtype=torch.int32, device="cuda")
+    itk.set_count_buffer(cnt)
+    itk.set_route_buffer(rb)
+    try:
+        idx, sc = itk.indexer_topk_fused(Q, K, W, kvt, k, k_scale=S, flags=case.flags)
+        torch.cuda.synchronize()
+    finally:
+        itk.set_count_buffer(None)
+        itk.set_route_buffer(None)
+    check_fused_rows(case, range(T), idx.cpu().numpy(), sc.cpu().numpy())
+    c, r = cnt.cpu().numpy(), rb.cpu().numpy()
+    print("counts", c.tolist(), "routes", r.tolist())
+    for t in range(T):
+        L = int(min(max(kv[t], 0), N))
+        if r[t] == 1:
+            assert c[t] >= min(k, L), (t, c[t])
+        if r[t] == 4:
+            assert c[t] == L, (t, c[t], L)
