@@ -55,6 +55,8 @@ def _load():
         lib.ora_fused_score_row.argtypes = [P, I, P, I, P, P, I64, I, I, U32, I, I64, P]
         lib.ora_fused_score_row.restype = I64
         lib.ora_topk_ragged.argtypes = [P, I64, P, P, I, I, P, P, I]
+        lib.ora_prior_from_topk.argtypes = [P, I64, I, I64, I, P]
+        lib.ora_prior_from_topk.restype = I
         lib.ora_topk_ragged.restype = I
         _lib = lib
     return _lib
@@ -184,3 +186,18 @@ def topk_ragged(case, rows: Optional[Sequence[int]] = None, nthreads: Optional[i
     if rc != 0:
         raise RuntimeError(f"ora_topk_ragged failed: {rc}")
     return idx, n
+
+
+def prior_from_topk(prev_idx: np.ndarray, N: int, k_prime: int) -> np.ndarray:
+    """History sample (LiteTopK Sec. 3.2 "Sampling"): the ``k_prime`` keys
+    that occur most often in the previous chunk's Top-k lists ``prev_idx``
+    [T_prev, k] (count descending, index ascending; entries outside [0, N)
+    ignored), padded with -1 past min(k_prime, N), in that order."""
+    prev = np.ascontiguousarray(prev_idx, dtype=np.int32)
+    if prev.ndim != 2:
+        raise ValueError("prev_idx must be [T_prev, k]")
+    out = np.empty(k_prime, dtype=np.int32)
+    n = _load().ora_prior_from_topk(_ptr(prev), prev.shape[0], prev.shape[1], N, k_prime, _ptr(out))
+    if n < 0:
+        raise RuntimeError(f"ora_prior_from_topk failed ({n})")
+    return out

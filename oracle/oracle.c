@@ -38,6 +38,14 @@
  *    first min(k, L).  Equal scores (including -0 == +0) go to the lower
  *    index.  Output slots past min(k, L) hold index -1.
  *
+ *  - History sample (LiteTopK Sec. 3.2 "Sampling"): the k' keys that occur
+ *    most often in the previous chunk's Top-k lists.  Count, for every key
+ *    j in [0, N), the entries of the previous lists equal to j (entries
+ *    outside [0, N), such as -1 padding, count for nothing); sort the keys by
+ *    (count descending, index ascending) and keep the first min(k', N).
+ *    Output slots past that hold -1.  The prior only places the initial gate
+ *    of the fused call; it never changes the fused Top-k.
+ *
  * Formats (decoded from their definitions, not by bit reinterpretation):
  *  - bf16: 1 sign, 8 exponent (bias 127), 7 fraction bits.
  *  - fp16 (IEEE-754 binary16): 1 sign, 5 exponent (bias 15), 10 fraction bits.
@@ -460,4 +468,26 @@ int ora_topk_ragged(const float *scores, int64_t pitch, const int32_t *row_len,
     j.out_idx = out_idx; j.out_n = out_n;
     j.maxL = pitch;
     return run_threads(&j, ragged_worker, nthreads);
+}
+
+/* History sample: the k_prime most frequent keys of the previous chunk's
+ * Top-k lists prev_idx[T_prev][k] (count descending, index ascending). */
+int ora_prior_from_topk(const int32_t *prev_idx, int64_t T_prev, int k, int64_t N, int k_prime,
+                        int32_t *out)
+{
+    if (T_prev < 0 || k <= 0 || N <= 0 || k_prime <= 0) return -1;
+    vi_t *buf = (vi_t *)malloc(sizeof(vi_t) * (size_t)N);
+    if (!buf) return -2;
+    for (int64_t j = 0; j < N; ++j) { buf[j].v = 0.0; buf[j].i = j; }
+    for (int64_t e = 0; e < T_prev * (int64_t)k; ++e) {
+        const int64_t j = prev_idx[e];
+        if (j >= 0 && j < N) buf[j].v += 1.0;
+    }
+    int32_t *tmp = (int32_t *)malloc(sizeof(int32_t) * (size_t)k_prime);
+    if (!tmp) { free(buf); return -2; }
+    const int n = select_sorted(buf, N, k_prime, tmp, NULL);
+    memcpy(out, tmp, sizeof(int32_t) * (size_t)k_prime);
+    free(tmp);
+    free(buf);
+    return n;
 }

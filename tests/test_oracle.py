@@ -403,3 +403,44 @@ def test_fp8_scoring_within_quantization_bound():
         err = np.abs(quant[t] - exact[t])
         assert (err <= bound * (1 + 1e-12)).all()
         assert err.max() > 0 and np.median(err / np.maximum(np.abs(exact[t]), 1e-12)) < 0.05
+
+
+# ---- history sample (LiteTopK Sec. 3.2 "Sampling": the k' keys most frequent
+# in the previous chunk's Top-k lists)
+
+def test_prior_worked_example():
+    """Counts by hand: key 1 three times, key 3 twice, keys 4 and 5 once,
+    keys 0 and 2 never; -1 padding and the out-of-range 9 count for nothing.
+    Equal counts go to the lower index, and slots past N hold -1."""
+    prev = np.array([[3, 1, -1], [1, 4, 3], [5, 1, 9]], dtype=np.int32)
+    assert oracle.prior_from_topk(prev, 6, 4).tolist() == [1, 3, 4, 5]
+    assert oracle.prior_from_topk(prev, 6, 5).tolist() == [1, 3, 4, 5, 0]
+    assert oracle.prior_from_topk(prev, 6, 8).tolist() == [1, 3, 4, 5, 0, 2, -1, -1]
+    # a key range that ends below the listed keys drops them
+    assert oracle.prior_from_topk(prev, 4, 4).tolist() == [1, 3, 0, 2]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prior_against_counter_brute_force(seed):
+    import collections
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(5, 200))
+    T, k = int(rng.integers(1, 12)), int(rng.integers(1, 20))
+    prev = rng.integers(-3, N + 3, size=(T, k)).astype(np.int32)
+    cnt = collections.Counter(int(j) for j in prev.ravel() if 0 <= j < N)
+    order = sorted(range(N), key=lambda j: (-cnt[j], j))
+    for kp in (1, 3, N // 2 + 1, N, N + 5):
+        want = order[:min(kp, N)] + [-1] * max(0, kp - N)
+        assert oracle.prior_from_topk(prev, N, kp).tolist() == want
+
+
+def test_prior_of_disjoint_lists_is_most_repeated_first():
+    """Each key of block b appears in b + 1 of the lists, so the blocks come
+    out in decreasing repetition, each in index order."""
+    N, k = 40, 8
+    rows = []
+    for b in range(4):  # keys 8b .. 8b+7 appear in b+1 rows
+        rows += [np.arange(8 * b, 8 * b + 8, dtype=np.int32)] * (b + 1)
+    prev = np.stack(rows)
+    got = oracle.prior_from_topk(prev, N, 32).tolist()
+    assert got == list(range(24, 32)) + list(range(16, 24)) + list(range(8, 16)) + list(range(0, 8))
