@@ -156,6 +156,61 @@ itk_status indexer_topk_fused(const void *Q, itk_dtype q_t, const void *K, itk_d
                               uint32_t flags, int32_t *out_idx, float *out_score,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Fused call with a history sample.
+ *
+ * Same operation, arguments and result as indexer_topk_fused; the initial
+ * gate comes from a caller-given list of keys instead of the strided view
+ * (LiteTopK, arXiv 2607.11976, Sec. 3.2 "Sampling"): the keys of the previous
+ * chunk's Top-k lists that occur most often (indexer_prior_from_topk below
+ * makes that list; about 3k entries for sparse attention).  Every query
+ * scores the listed keys below its own length; since they are keys of its
+ * own row, the k-th largest of their scores cannot exceed the row's k-th
+ * largest, and the gate is placed at the bin holding it, so every key of the
+ * Top-k passes.
+ *
+ *   prior_idx  [n_prior] int32 (device) key indices, any order.  Entries
+ *              outside [0, N) are ignored; a key listed twice is scored twice
+ *              and weakens the gate's guarantee, never the result.
+ *   n_prior    0 <= n_prior <= 65536; 0 gives the strided view, as
+ *              indexer_topk_fused does.  A query with fewer than k listed
+ *              keys below its length gets no gate (all its keys are
+ *              candidates, resolved by the recovery passes).
+ *   Rejected with ITK_ERR_UNSUPPORTED on the single-head path (H == 1 with
+ *   16-bit Q): LiteTopK keeps the history sample for sparse attention and
+ *   samples k-NN rows, which have no such temporal structure.
+ *   The workspace size depends on n_prior.
+ * ------------------------------------------------------------------------ */
+size_t indexer_topk_fused_prior_workspace_size(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k,
+                                               itk_dtype q_t, itk_dtype k_t, uint32_t flags, int32_t n_prior);
+
+itk_status indexer_topk_fused_prior(const void *Q, itk_dtype q_t, const void *K, itk_dtype k_t,
+                                    const float *k_scale, const float *W, const int32_t *kv_len,
+                                    int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, uint32_t flags,
+                                    const int32_t *prior_idx, int32_t n_prior,
+                                    int32_t *out_idx, float *out_score,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* The history sample of the next chunk (LiteTopK Sec. 3.2 "Sampling"): the
+ * k_prime keys that occur most often in the previous chunk's lists.
+ *
+ *   prev_idx   [T_prev, k] int32 (device): the previous chunk's out_idx.
+ *              Entries outside [0, N) (the -1 padding) count for nothing.
+ *   prior_out  [k_prime] int32: the keys sorted by (count descending, index
+ *              ascending), first min(k_prime, N) of them, in unspecified
+ *              order; slots past min(k_prime, N) hold -1.
+ *   Requires T_prev * k <= 2^24 (counts exact in fp32; ITK_ERR_UNSUPPORTED
+ *   otherwise), T_prev >= 0, k > 0, 0 < N <= 2^31 - 1, k_prime > 0.
+ *   Scratch: indexer_prior_workspace_size bytes (about 4 N plus the ragged
+ *   Top-k of one row of N).  Can run on its own stream, beside the current
+ *   chunk's work.
+ */
+size_t indexer_prior_workspace_size(int32_t T_prev, int32_t k, int64_t N, int32_t k_prime);
+
+itk_status indexer_prior_from_topk(const int32_t *prev_idx, int32_t T_prev, int32_t k, int64_t N,
+                                   int32_t k_prime, int32_t *prior_out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *itk_status_string(itk_status status);
 

@@ -61,6 +61,16 @@ def lib():
         L.indexer_topk_fused.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, P, P, I32, I32, I32, I64, I32, U32,
                                          P, P, P, SZ, P]
         L.indexer_topk_fused.restype = ctypes.c_int
+        L.indexer_topk_fused_prior_workspace_size.argtypes = [I32, I32, I32, I64, I32, ctypes.c_int, ctypes.c_int,
+                                                              U32, I32]
+        L.indexer_topk_fused_prior_workspace_size.restype = SZ
+        L.indexer_topk_fused_prior.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, P, P, I32, I32, I32, I64, I32,
+                                               U32, P, I32, P, P, P, SZ, P]
+        L.indexer_topk_fused_prior.restype = ctypes.c_int
+        L.indexer_prior_workspace_size.argtypes = [I32, I32, I64, I32]
+        L.indexer_prior_workspace_size.restype = SZ
+        L.indexer_prior_from_topk.argtypes = [P, I32, I32, I64, I32, P, P, SZ, P]
+        L.indexer_prior_from_topk.restype = ctypes.c_int
         L.itk_status_string.argtypes = [ctypes.c_int]
         L.itk_status_string.restype = ctypes.c_char_p
         L.itk_last_hip_error.argtypes = []
@@ -180,6 +190,57 @@ def indexer_topk_fused(Q, K, W, kv_len, k: int, k_scale=None, flags: int = 0, ou
                                   _stream(stream))
     _check(st, "indexer_topk_fused")
     return out_idx, out_score
+
+
+def fused_prior_workspace_size(T, H, D, N, k, q_t, k_t, flags, n_prior) -> int:
+    return int(lib().indexer_topk_fused_prior_workspace_size(T, H, D, N, k, q_t, k_t, flags, n_prior))
+
+
+def indexer_topk_fused_prior(Q, K, W, kv_len, k: int, prior, k_scale=None, flags: int = 0, out_idx=None,
+                             out_score=None, workspace=None, stream=None):
+    """indexer_topk_fused with a history sample: ``prior`` is an int32 device
+    tensor of key indices (the previous chunk's most frequent keys)."""
+    import torch
+    T, H, D = Q.shape
+    N = K.shape[0]
+    q_t, k_t = _dtype_code(Q), _dtype_code(K)
+    n_prior = int(prior.numel()) if prior is not None else 0
+    if prior is not None and (prior.dtype != torch.int32 or not prior.is_contiguous()):
+        raise TypeError("prior must be a contiguous int32 tensor")
+    if out_idx is None:
+        out_idx = torch.empty((T, k), dtype=torch.int32, device=Q.device)
+    if out_score is None:
+        out_score = torch.empty((T, k), dtype=torch.float32, device=Q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, fused_prior_workspace_size(T, H, D, N, k, q_t, k_t, flags, n_prior)),
+                                dtype=torch.uint8, device=Q.device)
+    st = lib().indexer_topk_fused_prior(_ptr(Q), q_t, _ptr(K), k_t, _ptr(k_scale), _ptr(W), _ptr(kv_len), T, H, D,
+                                        N, k, flags, _ptr(prior), n_prior, _ptr(out_idx), _ptr(out_score),
+                                        _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "indexer_topk_fused_prior")
+    return out_idx, out_score
+
+
+def prior_workspace_size(T_prev, k, N, k_prime) -> int:
+    return int(lib().indexer_prior_workspace_size(T_prev, k, N, k_prime))
+
+
+def prior_from_topk(prev_idx, N: int, k_prime: int, out=None, workspace=None, stream=None):
+    """The k_prime most frequent keys of the previous chunk's lists
+    ``prev_idx`` (int32 [T_prev, k], device); returns int32 [k_prime]."""
+    import torch
+    if prev_idx.dtype != torch.int32 or prev_idx.dim() != 2 or not prev_idx.is_contiguous():
+        raise TypeError("prev_idx must be a contiguous int32 [T_prev, k] tensor")
+    T_prev, k = prev_idx.shape
+    if out is None:
+        out = torch.empty(k_prime, dtype=torch.int32, device=prev_idx.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, prior_workspace_size(T_prev, k, N, k_prime)), dtype=torch.uint8,
+                                device=prev_idx.device)
+    st = lib().indexer_prior_from_topk(_ptr(prev_idx), T_prev, k, N, k_prime, _ptr(out), _ptr(workspace),
+                                       workspace.numel(), _stream(stream))
+    _check(st, "indexer_prior_from_topk")
+    return out
 
 
 def fused_tensors(case, device="cuda"):

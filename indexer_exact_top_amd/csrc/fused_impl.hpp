@@ -171,6 +171,14 @@ struct FusedArgs {
     // single-head (query-column) path
     float *gate;       // [T] admission gate (score space)
     uint32_t *qcnt;    // [T][P] candidates per (query, key split); may exceed capS
+    // history sample (head rows): the caller's prior key list, gathered
+    const int32_t *prior;  // [n_prior] caller's key indices, or null
+    int32_t *pidx;         // [np] gathered key index per entry, INT32_MAX where unusable; null = strided view
+    void *Kp;              // [np] key rows of the entries (zero rows where unusable)
+    float *kp_scale;       // [np] their FP8 scales (FP8 keys)
+    uint32_t *pcount;      // [T] entries below the query's length
+    int64_t np;            // entries, padded to whole tiles
+    int32_t n_prior, rowb; // listed entries; bytes per key row
     int64_t N, span, span_s, samp_cap;
     int32_t T, H, k, cap, capS, G, P, Ps, sample_tiles, force;
     float rho;
@@ -197,14 +205,28 @@ __device__ __forceinline__ void map_group_split(int b, int G, int P, int &g, int
 }
 
 // Number of sampled keys below L and the sample rank for the row.
+//
+// Strided view: the gate bin is the one holding the view's rank-q0 score,
+// q0 = ceil(rho k n_a / L), which aims at about rho k admitted keys.
+// History sample (LiteTopK Sec. 3.2 "Sampling"): the sample is a set of the
+// row's own keys, so its k-th largest score cannot exceed the row's k-th
+// largest, and the gate bin is the one holding that k-th sample score (q0 =
+// k): every key of the row's Top-k passes it.  A row with fewer than k usable
+// entries (or a degenerate sampled range) gets no gate.
 struct RowSample {
     uint32_t n_a;
     bool admit_all;
     uint32_t q0;
 };
-__device__ __forceinline__ RowSample row_sample(const FusedArgs &a, int g, uint32_t L, bool degenerate)
+__device__ __forceinline__ RowSample row_sample(const FusedArgs &a, int t, int g, uint32_t L, bool degenerate)
 {
     RowSample rs;
+    if (a.pidx) {
+        rs.n_a = a.pcount[t];
+        rs.q0 = (uint32_t)a.k;
+        rs.admit_all = degenerate || rs.n_a < (uint32_t)a.k;
+        return rs;
+    }
     const uint32_t st = (uint32_t)a.sample_tiles, phase = (uint32_t)g % st;
     const uint32_t nt = (L + TILE_KEYS - 1) / TILE_KEYS;
     const uint32_t ns = nt > phase ? (nt - 1u - phase) / st + 1u : 0u;
@@ -837,6 +859,31 @@ __device__ __forceinline__ uint32_t group_max_len(const FusedArgs &a, int g)
     return m;
 }
 
+// ------------------------------------------- history sample: gather rows
+// Entry e < n_prior of the caller's list names key prior[e]; entries outside
+// [0, N) (and the padding up to whole tiles) are unusable.  Each thread moves
+// one 16-byte chunk of an entry's key row into the gathered copy, which the
+// sample passes then scan like K; unusable entries get a zero row and the
+// index INT32_MAX, which no row's length exceeds.
+template <class C>
+__global__ __launch_bounds__(256) void k_prior_gather(FusedArgs a)
+{
+    constexpr int ch = C::D * C::kbytes / 16;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t e = gid / ch;
+    const int c = (int)(gid - e * ch);
+    if (e >= a.np) return;
+    const int64_t j = e < a.n_prior ? (int64_t)a.prior[e] : -1;
+    const bool ok = j >= 0 && j < a.N;
+    const u32x4_t v = ok ? *reinterpret_cast<const u32x4_t *>(static_cast<const char *>(a.K) + j * a.rowb + c * 16)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t *>(static_cast<char *>(a.Kp) + e * a.rowb + c * 16) = v;
+    if (c == 0) {
+        a.pidx[e] = ok ? (int32_t)j : 0x7FFFFFFF;
+        if (a.kp_scale) a.kp_scale[e] = ok ? a.k_scale[j] : 0.f;
+    }
+}
+
 // -------------------------------------------- sample pass A: score range
 template <class C>
 __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
@@ -856,9 +903,20 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
         if (lane == 0) {
             a.tail[t] = 0u;
             a.rflag[t] = 0u;
+            if (a.pidx) a.pcount[t] = 0u;
         }
     }
-    const uint32_t maxL = group_max_len(a, g);
+    // History sample: the scan runs over the gathered entries (their key rows
+    // stand in for K), and entry e is usable for the row when its key is
+    // below the row's length.
+    const bool prior = a.pidx != nullptr;
+    FusedArgs sa = a;
+    if (prior) {
+        sa.K = a.Kp;
+        sa.k_scale = a.kp_scale;
+        sa.N = a.np;
+    }
+    const uint32_t maxL = prior ? (uint32_t)a.np : group_max_len(a, g);
     const SampleIter it = sample_iter(a, g, p, maxL);
     QFrags<C> qf;
     if (active) qf.load(a, t);
@@ -868,8 +926,9 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
     // that pass B bins them without scoring the view again.
     const int64_t phase = g % a.sample_tiles;
     float *srow = a.samp ? a.samp + (size_t)(active ? t : 0) * a.samp_cap : nullptr;
-    scan_tiles<C, 1>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, it.end, active, L, [&](int64_t key0, float s) {
-        const bool valid = key0 + lane < (int64_t)L;
+    const uint32_t Lscan = prior ? (uint32_t)a.np : L;
+    scan_tiles<C, 1>(sa, tb, qf, it.first_key, it.stride_keys, it.ntiles, it.end, active, Lscan, [&](int64_t key0, float s) {
+        const bool valid = prior ? a.pidx[key0 + lane] < (int32_t)L : key0 + lane < (int64_t)L;
         if (valid) {
             mn = fminf(mn, s);
             mx = fmaxf(mx, s);
@@ -928,7 +987,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
         bp = bin_params(a, t);
         if (p == 0 && lane == 0) a.param[t] = bp;
     }
-    const uint32_t maxL = group_max_len(a, g);
+    const bool prior = a.pidx != nullptr;
+    const uint32_t maxL = prior ? (uint32_t)a.np : group_max_len(a, g);
     const SampleIter it = sample_iter(a, g, p, maxL);
     // a degenerate sampled range leaves the gate open: nothing to count
     const bool count = active && bp.z == 0.f;
@@ -941,7 +1001,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
                          });
     } else if (count) {
         // the tiles pass A visited: first_key + i * stride below min(end, L)
-        const int64_t kend = it.end < (int64_t)L ? it.end : (int64_t)L;
+        // (a history sample stores every entry of the split, NaN where unusable)
+        const int64_t kend = prior || it.end < (int64_t)L ? it.end : (int64_t)L;
         const int64_t phase = g % a.sample_tiles;
         const float *srow = a.samp + (size_t)t * a.samp_cap;
         int n = 0;
@@ -950,6 +1011,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
         if (n > it.ntiles) n = it.ntiles;
         const int64_t j0 = (it.first_key / TILE_KEYS - phase) / a.sample_tiles;  // first sampled tile's slot
         constexpr int B = 8;  // loads in flight per lane
+        uint32_t usable = 0;
         for (int i0 = 0; i0 < n; i0 += B) {
             float v[B];
 #pragma unroll
@@ -957,7 +1019,14 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
                 v[j] = i0 + j < n ? srow[(j0 + i0 + j) * TILE_KEYS + lane] : __builtin_nanf("");
 #pragma unroll
             for (int j = 0; j < B; ++j)
-                if (v[j] == v[j]) atomicAdd(&whist[wave][bin_of(fmaf(v[j], bp.y, bp.x))], 1u);
+                if (v[j] == v[j]) {
+                    atomicAdd(&whist[wave][bin_of(fmaf(v[j], bp.y, bp.x))], 1u);
+                    ++usable;
+                }
+        }
+        if (prior) {
+            usable = lane_value(wave_incl_sum(usable), 63);
+            if (lane == 0 && usable) atomicAdd(&a.pcount[t], usable);
         }
     }
     __syncthreads();
@@ -1002,7 +1071,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
     float gate_f = -__builtin_inff();
     if (active) {
         const float4 bp = a.param[t];
-        const RowSample rs = row_sample(a, g, L, bp.z != 0.f);
+        const RowSample rs = row_sample(a, t, g, L, bp.z != 0.f);
         if (!rs.admit_all) {
             off = bp.x;
             delta = bp.y;
@@ -1213,7 +1282,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main_kp(FusedArgs a)
     float gate_f = -__builtin_inff();
     {
         const float4 bp = a.param[t];
-        const RowSample rs = row_sample(a, t / FUSED_WAVES, L, bp.z != 0.f);
+        const RowSample rs = row_sample(a, t, t / FUSED_WAVES, L, bp.z != 0.f);
         if (!rs.admit_all) {
             off = bp.x;
             delta = bp.y;
@@ -1524,7 +1593,7 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
     if (tid == 0 && a.count) a.count[t] = (int32_t)n;
     if (tid == 0 && a.route) {
         const float4 bp = a.param[t];
-        const RowSample rs = row_sample(a, t / FUSED_WAVES, L, bp.z != 0.f);
+        const RowSample rs = row_sample(a, t, t / FUSED_WAVES, L, bp.z != 0.f);
         a.route[t] = recover ? FROUTE_RECOVER
                              : (a.rflag[t] ? FROUTE_GRID_RECOVERY : (rs.admit_all ? FROUTE_ALL : FROUTE_SAMPLE));
     }
@@ -1537,7 +1606,13 @@ hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t 
     hipError_t e;
     {
         StageTimer st(ST_F_MINMAX, stream);
-        e = launch_kernel(k_fused_minmax<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a);
+        e = hipSuccess;
+        if (a.pidx) {
+            const int64_t threads = p.np * (a.rowb / 16);
+            e = launch_kernel(k_prior_gather<C>, dim3((unsigned)((threads + 255) / 256)), dim3(256), stream, a);
+        }
+        if (e == hipSuccess)
+            e = launch_kernel(k_fused_minmax<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a);
     }
     if (e != hipSuccess) return e;
     {

@@ -284,7 +284,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_gate(FusedArgs a)
     const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const uint32_t L = kv_length(a, t);
     const int g = t / QROW_Q;
-    const RowSample rs = row_sample(a, g, L, false);
+    const RowSample rs = row_sample(a, t, g, L, false);
     // per-call reset of the query's slice counters
     for (int p = tid; p < 2 * a.P; p += NT) a.qcnt[(size_t)t * a.P * 2 + p] = 0u;
     if (rs.admit_all) {

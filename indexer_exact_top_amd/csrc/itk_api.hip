@@ -82,9 +82,10 @@ StageTimer::~StageTimer()
 static uint64_t ceil_div_u(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk_dtype qt, itk_dtype kt,
-                      uint32_t flags, FusedPlan *out)
+                      uint32_t flags, FusedPlan *out, int32_t n_prior)
 {
-    if (T <= 0 || H <= 0 || D <= 0 || N <= 0 || k <= 0) return ITK_ERR_INVALID_ARG;
+    if (T <= 0 || H <= 0 || D <= 0 || N <= 0 || k <= 0 || n_prior < 0) return ITK_ERR_INVALID_ARG;
+    if (n_prior > PRIOR_MAX) return ITK_ERR_UNSUPPORTED;
     if (N > (int64_t)0x7FFFFFFF) return ITK_ERR_UNSUPPORTED;
     if (qt < ITK_F32 || qt > ITK_FP8_E4M3 || kt < ITK_F32 || kt > ITK_FP8_E4M3) return ITK_ERR_INVALID_ARG;
     if (flags & ~(ITK_FLAG_NO_RELU | ITK_FLAG_FP8_SCORE)) return ITK_ERR_INVALID_ARG;
@@ -107,6 +108,10 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     FusedPlan p;
     p.T = T; p.H = H; p.D = D; p.N = N; p.k = k; p.qt = qt; p.kt = kt; p.flags = flags; p.HB = HB;
     if (H == 1 && qt != ITK_F32 && find_qrow_launcher(qt, kt, D, relu)) {
+        // no history sample here: LiteTopK Sec. 3.2 keeps the history sample
+        // for sparse attention and samples k-NN rows, which carry no such
+        // temporal structure
+        if (n_prior > 0) return ITK_ERR_UNSUPPORTED;
         // Single head: queries are the MFMA columns (32 per block, QROW_Q per
         // workgroup); keys are split so that about 256 workgroups run.
         p.qrow = true;
@@ -198,6 +203,23 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     // keeps the workspace O(T k); a longer view is scored again by pass B.
     p.samp_cap = (int64_t)ceil_div_u((uint64_t)ntiles, (uint64_t)st) * TILE_KEYS;
     if (p.samp_cap > 2 * (int64_t)cap) p.samp_cap = 0;
+    if (n_prior > 0) {
+        // History sample: the sample passes scan the gathered entries (every
+        // one of them, scores stored), split so that about 256 workgroups
+        // run, with at least 4 tiles per split.
+        p.n_prior = n_prior;
+        p.np = (int64_t)ceil_div_u((uint64_t)n_prior, TILE_KEYS) * TILE_KEYS;
+        p.rowb = D * (kt == ITK_F32 ? 4 : (kt == ITK_FP8_E4M3 ? 1 : 2));
+        int Ps = p.G >= 256 ? 1 : (int)ceil_div_u(256, (uint64_t)p.G);
+        const int Psmax = (int)(p.np / (4 * TILE_KEYS)) > 1 ? (int)(p.np / (4 * TILE_KEYS)) : 1;
+        if (Ps > Psmax) Ps = Psmax;
+        int64_t span_s = (int64_t)ceil_div_u((uint64_t)p.np, (uint64_t)Ps);
+        span_s = (int64_t)ceil_div_u((uint64_t)span_s, TILE_KEYS) * TILE_KEYS;
+        p.Ps = (int32_t)ceil_div_u((uint64_t)p.np, (uint64_t)span_s);
+        p.span_s = span_s;
+        p.sample_tiles = 1;
+        p.samp_cap = p.np;
+    }
     size_t off = 0;
     p.off_param = off; off = align256(off + (size_t)T * sizeof(float4));
     p.off_mm = off; off = align256(off + (size_t)T * p.Ps * sizeof(float2));
@@ -208,13 +230,20 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     p.off_samp = off; off = align256(off + (size_t)T * p.samp_cap * sizeof(float));
     p.off_hist_r = off; off = align256(off + (size_t)T * NBINS * sizeof(uint32_t));
     p.off_rflag = off; off = align256(off + (size_t)T * sizeof(uint32_t));
+    if (n_prior > 0) {
+        p.off_pidx = off; off = align256(off + (size_t)p.np * sizeof(int32_t));
+        p.off_kp = off; off = align256(off + (size_t)p.np * p.rowb);
+        p.off_kps = off; off = align256(off + (size_t)p.np * sizeof(float));
+        p.off_pcount = off; off = align256(off + (size_t)T * sizeof(uint32_t));
+    }
     p.bytes = off;
     *out = p;
     return ITK_OK;
 }
 
 hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const float *k_scale, const float *W,
-                        const int32_t *kv_len, int32_t *out_idx, float *out_score, void *ws, hipStream_t stream)
+                        const int32_t *kv_len, int32_t *out_idx, float *out_score, void *ws, hipStream_t stream,
+                        const int32_t *prior)
 {
     char *w = static_cast<char *>(ws);
     FusedArgs a;
@@ -236,6 +265,18 @@ hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const 
     a.rflag = p.qrow ? nullptr : reinterpret_cast<uint32_t *>(w + p.off_rflag);
     a.samp_cap = p.samp_cap;
     a.gate = nullptr; a.qcnt = nullptr; a.capS = 0;
+    a.prior = nullptr; a.pidx = nullptr; a.Kp = nullptr; a.kp_scale = nullptr; a.pcount = nullptr;
+    a.np = 0; a.n_prior = 0; a.rowb = p.rowb;
+    if (p.n_prior > 0) {
+        if (!prior || p.qrow) return hipErrorInvalidValue;
+        a.prior = prior;
+        a.n_prior = p.n_prior;
+        a.np = p.np;
+        a.pidx = reinterpret_cast<int32_t *>(w + p.off_pidx);
+        a.Kp = w + p.off_kp;
+        a.kp_scale = k_scale ? reinterpret_cast<float *>(w + p.off_kps) : nullptr;
+        a.pcount = reinterpret_cast<uint32_t *>(w + p.off_pcount);
+    }
     if (p.qrow) {
         a.gate = reinterpret_cast<float *>(w + p.off_gate);
         a.qcnt = reinterpret_cast<uint32_t *>(w + p.off_qcnt);
@@ -325,6 +366,53 @@ itk_status indexer_topk_fused(const void *Q, itk_dtype q_t, const void *K, itk_d
     const hipError_t e = launch_fused(p, Q, K, k_scale, W, kv_len, out_idx, out_score, workspace,
                                       static_cast<hipStream_t>(stream));
     return hip_status(e);
+}
+
+size_t indexer_topk_fused_prior_workspace_size(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k,
+                                               itk_dtype q_t, itk_dtype k_t, uint32_t flags, int32_t n_prior)
+{
+    FusedPlan p;
+    if (plan_fused(T, H, D, N, k, q_t, k_t, flags, &p, n_prior) != ITK_OK) return 0;
+    return p.bytes;
+}
+
+itk_status indexer_topk_fused_prior(const void *Q, itk_dtype q_t, const void *K, itk_dtype k_t,
+                                    const float *k_scale, const float *W, const int32_t *kv_len, int32_t T,
+                                    int32_t H, int32_t D, int64_t N, int32_t k, uint32_t flags,
+                                    const int32_t *prior_idx, int32_t n_prior, int32_t *out_idx, float *out_score,
+                                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!Q || !K || !W || !kv_len || !out_idx || !out_score) return ITK_ERR_INVALID_ARG;
+    if ((k_t == ITK_FP8_E4M3) != (k_scale != nullptr)) return ITK_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(Q) & 15u) || (reinterpret_cast<uintptr_t>(K) & 15u)) return ITK_ERR_INVALID_ARG;
+    if (n_prior < 0 || (n_prior > 0 && !prior_idx)) return ITK_ERR_INVALID_ARG;
+    FusedPlan p;
+    const itk_status st = plan_fused(T, H, D, N, k, q_t, k_t, flags, &p, n_prior);
+    if (st != ITK_OK) return st;
+    if (!workspace || workspace_bytes < p.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return ITK_ERR_WORKSPACE;
+    const hipError_t e = launch_fused(p, Q, K, k_scale, W, kv_len, out_idx, out_score, workspace,
+                                      static_cast<hipStream_t>(stream), prior_idx);
+    return hip_status(e);
+}
+
+size_t indexer_prior_workspace_size(int32_t T_prev, int32_t k, int64_t N, int32_t k_prime)
+{
+    PriorPlan p;
+    if (plan_prior(T_prev, k, N, k_prime, &p) != ITK_OK) return 0;
+    return p.bytes;
+}
+
+itk_status indexer_prior_from_topk(const int32_t *prev_idx, int32_t T_prev, int32_t k, int64_t N, int32_t k_prime,
+                                   int32_t *prior_out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!prior_out || (T_prev > 0 && !prev_idx)) return ITK_ERR_INVALID_ARG;
+    PriorPlan p;
+    const itk_status st = plan_prior(T_prev, k, N, k_prime, &p);
+    if (st != ITK_OK) return st;
+    if (!workspace || workspace_bytes < p.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return ITK_ERR_WORKSPACE;
+    return hip_status(launch_prior(p, prev_idx, prior_out, workspace, static_cast<hipStream_t>(stream)));
 }
 
 itk_status itk_set_plan_opts(const itk_plan_opts *o)

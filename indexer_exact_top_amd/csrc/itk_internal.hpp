@@ -152,12 +152,28 @@ struct FusedPlan {
     size_t off_param = 0, off_mm = 0, off_hist = 0, off_tail = 0, off_gate = 0, off_cand = 0;
     size_t off_hist_r = 0, off_rflag = 0;
     size_t off_samp = 0, off_qcnt = 0, bytes = 0;
+    // history sample (head rows only): listed entries, padded entries, key row bytes
+    int32_t n_prior = 0, rowb = 0;
+    int64_t np = 0;
+    size_t off_pidx = 0, off_kp = 0, off_kps = 0, off_pcount = 0;
 };
+// Largest history sample a fused call takes.
+constexpr int32_t PRIOR_MAX = 1 << 16;
 itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk_dtype qt, itk_dtype kt,
-                      uint32_t flags, FusedPlan *out);
+                      uint32_t flags, FusedPlan *out, int32_t n_prior = 0);
 hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const float *k_scale,
                         const float *W, const int32_t *kv_len, int32_t *out_idx, float *out_score,
-                        void *ws, hipStream_t stream);
+                        void *ws, hipStream_t stream, const int32_t *prior = nullptr);
+// History sample from the previous chunk's lists (count buffer + ragged Top-k).
+struct PriorPlan {
+    int64_t N = 0;
+    int32_t T_prev = 0, k = 0, k_prime = 0;
+    RaggedPlan rag;
+    size_t off_count = 0, off_rag = 0, bytes = 0;
+};
+itk_status plan_prior(int32_t T_prev, int32_t k, int64_t N, int32_t k_prime, PriorPlan *out);
+hipError_t launch_prior(const PriorPlan &p, const int32_t *prev_idx, int32_t *prior_out, void *ws,
+                        hipStream_t stream);
 
 // ------------------------------------------------------------ profiling
 // Records an event pair around a launch when profiling is enabled.

@@ -36,6 +36,7 @@ FP8_E4M3_MAX = 448.0
 __all__ = [
     "F32", "BF16", "F16", "FP8_E4M3", "FLAG_NO_RELU", "FusedCase", "RaggedCase",
     "gen_fused", "gen_fused_exact", "gen_ragged", "fused_config", "ragged_config", "csa_chunk", "CONFIGS",
+    "prefill_chunk_pair",
     "encode", "decode_reference_free",
 ]
 
@@ -338,6 +339,45 @@ def csa_chunk(S: int, chunk: int, *, m: int = 4, k: int = 2048, H: int = 64, D: 
     kv = (np.arange(t0, t0 + chunk, dtype=np.int64) + 1) // m
     return gen_fused(chunk, H, D, N, k, q_dtype=BF16, k_dtype=BF16, kv_len=kv.astype(np.int32),
                      seed=seed, name=f"csa_chunk_S{S}_m{m}")
+
+
+def prefill_chunk_pair(T, H, D, N, k, *, start: Optional[int] = None, n_hot: Optional[int] = None,
+                       k_dtype=BF16, seed: int = 707, name: str = "prefill_chunk_pair"):
+    """Two consecutive query chunks of one prefill over shared keys, with the
+    temporal structure that LiteTopK Sec. 3.2 ("Sampling") relies on:
+    adjacent chunks attend to the same prefix tokens.
+
+    Every head h has a fixed direction u_h (a unit Gaussian vector).  Keys are
+    N(0, I)/sqrt(D); ``n_hot`` of them (default 3k), drawn at random, each get
+    a_j * u_h added for a random head h and a_j ~ U(0.5, 1.5), so that they
+    score high for every query.  Query rows of both chunks are
+    u_h + N(0, I)/sqrt(D); W ~ U(0,1)/H.  The current chunk's T query tokens
+    sit at positions start .. start+T-1 (default: the last T keys) and the
+    previous chunk's at the T positions before; a token at position p sees
+    kv_len = p + 1 keys (capped at N).  Returns (previous, current) cases
+    with the same K (and FP8 scales)."""
+    rng = _rng(seed)
+    n_hot = 3 * k if n_hot is None else n_hot
+    u = _normal_rows(rng, H, D, True)
+    kf = _normal_rows(rng, N, D, False)
+    hot = rng.choice(N, size=min(n_hot, N), replace=False)
+    kf[hot] += (rng.uniform(0.5, 1.5, size=hot.size)[:, None] * u[rng.integers(0, H, size=hot.size)]).astype(np.float32)
+    k_scale = None
+    if k_dtype == FP8_E4M3:
+        amax = np.abs(kf).max(axis=1)
+        k_scale = np.where(amax > 0, amax / np.float32(FP8_E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        kf = kf / k_scale[:, None]
+    k_bits = encode(kf, k_dtype)
+    start = N - T if start is None else start
+    cases = []
+    for c, p0 in enumerate((start - T, start)):
+        q = (u[None, :, :] + _normal_rows(rng, T * H, D, False).reshape(T, H, D)).astype(np.float32)
+        W = (rng.random((T, H), dtype=np.float32) * np.float32(1.0 / H)).astype(np.float32)
+        kv = np.minimum(np.arange(p0, p0 + T, dtype=np.int64) + 1, N).astype(np.int32)
+        cases.append(FusedCase(name=f"{name}_{'prev' if c == 0 else 'cur'}", T=T, H=H, D=D, N=N, k=k,
+                               q_dtype=BF16, k_dtype=k_dtype, q_bits=encode(q, BF16), k_bits=k_bits,
+                               k_scale=k_scale, W=W, kv_len=kv))
+    return cases[0], cases[1]
 
 
 CONFIGS = {

@@ -126,3 +126,37 @@ def test_plan_opts_validation():
     # the row-local route (many rows of at most 2^18 scores) needs no scratch beyond a token
     assert lib.topk_ragged_workspace_size(1024, 131072, 2048) <= 256
     assert lib.itk_set_plan_opts(ctypes.byref(itk.PlanOpts(0, 0, 0, 0, 0, 0, 3))) == 1
+
+
+def test_history_sample_validation():
+    lib = itk.lib()
+    BF, F16 = itk.BF16, itk.F16
+    wsz = lib.indexer_topk_fused_prior_workspace_size
+    base = lib.indexer_topk_fused_workspace_size(64, 64, 128, 133120, 2048, BF, BF, 0)
+    # no list: the strided view's plan; a list adds its gathered rows (O(n_prior))
+    assert wsz(64, 64, 128, 133120, 2048, BF, BF, 0, 0) == base
+    w6 = wsz(64, 64, 128, 133120, 2048, BF, BF, 0, 6144)
+    assert base < w6 < base + 6144 * (256 + 8) + 64 * 4 + 4 * 256 + 2 * 64 * 2048 * 4
+    assert wsz(64, 64, 128, 133120, 2048, BF, BF, 0, 1 << 16) > 0
+    assert wsz(64, 64, 128, 133120, 2048, BF, BF, 0, (1 << 16) + 1) == 0   # above the largest list
+    assert wsz(64, 64, 128, 133120, 2048, BF, BF, 0, -1) == 0
+    assert wsz(64, 1, 256, 1 << 20, 2048, F16, F16, 1, 4096) == 0          # single-head path: no history
+    call = lambda n, pr=FAKE, H=64, D=128, qt=BF, fl=0: lib.indexer_topk_fused_prior(
+        FAKE, qt, FAKE, qt, None, FAKE, FAKE, 4, H, D, 1000, 16, fl, pr, n, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert call(-1) == 1
+    assert call(5, pr=None) == 1
+    assert call((1 << 16) + 1) == 2
+    assert call(64, H=1, D=256, qt=F16, fl=1) == 2
+    # the list builder
+    pw = lib.indexer_prior_workspace_size
+    assert pw(2048, 2048, 133120, 6144) > 4 * 133120
+    assert pw(8192, 2048, 1 << 20, 6144) > 0          # 2^24 list entries: counts still exact in fp32
+    assert pw(8193, 2048, 1 << 20, 6144) == 0
+    assert pw(-1, 2048, 1000, 10) == 0 and pw(1, 0, 1000, 10) == 0 and pw(1, 8, 0, 10) == 0
+    assert pw(1, 8, 1000, 0) == 0
+    pf = lib.indexer_prior_from_topk
+    need = pw(4, 8, 1000, 10)
+    assert pf(None, 4, 8, 1000, 10, FAKE, FAKE, need, None) == 1
+    assert pf(FAKE, 4, 8, 1000, 10, None, FAKE, need, None) == 1
+    assert pf(FAKE, 4, 8, 1000, 10, FAKE, FAKE, need - 1, None) == 3
+    assert pf(FAKE, 4, 8, 1 << 31, 10, FAKE, FAKE, need, None) == 2
