@@ -196,14 +196,13 @@ itk_status indexer_topk_fused_prior(const void *Q, itk_dtype q_t, const void *K,
  *
  *   prev_idx   [T_prev, k] int32 (device): the previous chunk's out_idx.
  *              Entries outside [0, N) (the -1 padding) count for nothing.
- *   prior_out  [k_prime] int32: the keys sorted by (count descending, index
- *              ascending), first min(k_prime, N) of them, in unspecified
- *              order; slots past min(k_prime, N) hold -1.
- *   Requires T_prev * k <= 2^24 (counts exact in fp32; ITK_ERR_UNSUPPORTED
- *   otherwise), T_prev >= 0, k > 0, 0 < N <= 2^31 - 1, k_prime > 0.
- *   Scratch: indexer_prior_workspace_size bytes (about 4 N plus the ragged
- *   Top-k of one row of N).  Can run on its own stream, beside the current
- *   chunk's work.
+ *   prior_out  [k_prime] int32: of the keys sorted by (count descending,
+ *              index ascending), the first min(k_prime, N), written in
+ *              ascending index order; slots past min(k_prime, N) hold -1.
+ *   Requires T_prev * k < 2^25 (ITK_ERR_UNSUPPORTED otherwise), T_prev >= 0,
+ *   k > 0, 0 < N <= 2^31 - 1, k_prime > 0.
+ *   Scratch: indexer_prior_workspace_size bytes (4 N plus about 50 KB).
+ *   Can run on its own stream, beside the current chunk's work.
  */
 size_t indexer_prior_workspace_size(int32_t T_prev, int32_t k, int64_t N, int32_t k_prime);
 

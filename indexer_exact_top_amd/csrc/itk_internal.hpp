@@ -167,9 +167,8 @@ hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const 
 // History sample from the previous chunk's lists (count buffer + ragged Top-k).
 struct PriorPlan {
     int64_t N = 0;
-    int32_t T_prev = 0, k = 0, k_prime = 0;
-    RaggedPlan rag;
-    size_t off_count = 0, off_rag = 0, bytes = 0;
+    int32_t T_prev = 0, k = 0, k_prime = 0, nblk = 0;
+    size_t off_count = 0, off_h1 = 0, off_h2 = 0, off_blk = 0, off_par = 0, bytes = 0;
 };
 itk_status plan_prior(int32_t T_prev, int32_t k, int64_t N, int32_t k_prime, PriorPlan *out);
 hipError_t launch_prior(const PriorPlan &p, const int32_t *prev_idx, int32_t *prior_out, void *ws,

@@ -150,8 +150,8 @@ def test_history_sample_validation():
     # the list builder
     pw = lib.indexer_prior_workspace_size
     assert pw(2048, 2048, 133120, 6144) > 4 * 133120
-    assert pw(8192, 2048, 1 << 20, 6144) > 0          # 2^24 list entries: counts still exact in fp32
-    assert pw(8193, 2048, 1 << 20, 6144) == 0
+    assert pw(16383, 2048, 1 << 20, 6144) > 0         # counts stay below 2^25
+    assert pw(16384, 2048, 1 << 20, 6144) == 0
     assert pw(-1, 2048, 1000, 10) == 0 and pw(1, 0, 1000, 10) == 0 and pw(1, 8, 0, 10) == 0
     assert pw(1, 8, 1000, 0) == 0
     pf = lib.indexer_prior_from_topk

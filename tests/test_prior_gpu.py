@@ -39,7 +39,24 @@ def test_prior_from_topk_matches_oracle(itk, T, k, N, kp, seed):
     g = got.cpu().numpy()
     n = min(kp, N)
     assert (g[n:] == -1).all()
-    assert sorted(g[:n].tolist()) == sorted(want[:n].tolist())
+    # the list comes out in ascending index order
+    assert g[:n].tolist() == sorted(want[:n].tolist())
+
+
+@pytest.mark.parametrize("kp", [3, 8, 20])
+def test_prior_counts_above_4096(itk, kp):
+    """Counts in the second bin of the first histogram level and beyond
+    (5000 and 9000 repeats), ties at the boundary count, and padding."""
+    rng = np.random.default_rng(kp)
+    T, k, N = 9000, 8, 3000
+    prev = rng.integers(0, N, size=(T, k)).astype(np.int32)
+    prev[:, 0] = 17                       # 9000 occurrences
+    prev[:5000, 1] = 2999                 # 5000 and more
+    prev[:5000, 2] = 5                    # a tie with 2999 at 5000 (before the random hits)
+    prev[5000:, 1] = 1000
+    want = oracle.prior_from_topk(prev, N, kp)
+    got = itk.prior_from_topk(torch.from_numpy(prev).cuda(), N, kp).cpu().numpy()
+    assert got.tolist() == sorted(want.tolist())
 
 
 def _fused(itk, case, prior, count=False, routes=False):
@@ -127,7 +144,7 @@ def test_consecutive_prefill_chunks(itk):
     torch.cuda.synchronize()
     # the prior is the oracle's definition applied to the kernel's own lists
     want = oracle.prior_from_topk(pidx.cpu().numpy(), prev.N, 3 * prev.k)
-    assert sorted(prior.cpu().numpy().tolist()) == sorted(want.tolist())
+    assert prior.cpu().numpy().tolist() == sorted(want.tolist())
     idx, sc, cnt, rt = _fused(itk, cur, prior.cpu().numpy(), count=True, routes=True)
     check_fused_rows(cur, range(cur.T), idx, sc)
     assert set(np.unique(rt).tolist()) <= {1}, np.bincount(rt).tolist()
