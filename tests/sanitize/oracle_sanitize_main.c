@@ -30,6 +30,7 @@ int64_t ora_fused_score_row(const void *Q, int q_t, const void *K, int k_t, cons
                             double *out);
 int ora_topk_ragged(const float *scores, int64_t pitch, const int32_t *row_len, const int32_t *rows, int nrows,
                     int k, int32_t *out_idx, int32_t *out_n, int nthreads);
+int ora_prior_from_topk(const int32_t *prev_idx, int64_t T_prev, int k, int64_t N, int k_prime, int32_t *out);
 
 #define CHECK(c)                                                        \
     do {                                                                \
@@ -103,6 +104,13 @@ int main(void)
     ora_encode_e4m3_array(codes, back, 256, 4);
     for (int c = 0; c < 256; ++c) CHECK(back[c] == c || (isnan(codes[c]) && (back[c] & 0x7F) == 0x7F));
     CHECK(ora_encode_e4m3(NAN) == 0x7F && ora_encode_e4m3(-INFINITY) == 0xFF && ora_encode_e4m3(465.0f) == 0x7F);
+
+    /* history list: -1 padding and keys outside [0, N), k' above N, no lists */
+    const int32_t prev[12] = {3, 1, -1, 1, 4, 3, 5, 1, 9, 2147483647, -2147483647 - 1, 0};
+    int32_t prior[10];
+    CHECK(ora_prior_from_topk(prev, 4, 3, 6, 10, prior) == 6 && prior[0] == 1 && prior[9] == -1);
+    CHECK(ora_prior_from_topk(prev, 0, 3, 6, 2, prior) == 2 && prior[0] == 0 && prior[1] == 1);
+    CHECK(ora_prior_from_topk(prev, 4, 3, 0, 2, prior) == -1);
 
     free(Q); free(Kf); free(K8); free(S); free(W); free(X);
     printf("oracle sanitizer run ok\n");
