@@ -102,7 +102,7 @@ struct RaggedPlan {
     bool rowlocal = false;   // one workgroup per row, candidates on chip
     int32_t rlcap = 0;       // row-local: on-chip candidate capacity
     // workspace carve
-    size_t off_cnt = 0, off_ep = 0, off_slices = 0, off_band = 0, bytes = 0;
+    size_t off_cnt = 0, off_ep = 0, off_slices = 0, off_band = 0, off_order = 0, bytes = 0;
 };
 RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k);
 hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t *row_len,

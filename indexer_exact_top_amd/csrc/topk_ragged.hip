@@ -64,6 +64,7 @@ struct RaggedArgs {
     int64_t pitch, seg;
     int32_t M, k, P, subcap, bandcap, view_blocks, force;
     int32_t rlcap;   // row-local route: candidates kept on chip (<= STASH_CAP)
+    int32_t *order;  // row-local route: [M] rows by descending length (workgroup b takes row order[b])
     float rho, rho1;
 };
 
@@ -456,6 +457,43 @@ __global__ __launch_bounds__(NT) void k_ragged_finish(RaggedArgs a, int vec)
 // ------------------------------------------------------------ row-local
 // One workgroup of RL_THREADS per row (see the header).  Chunks of RL_U
 // 16-byte loads per thread are double-buffered in registers.
+// Longest rows first: workgroup b of the row-local pass takes row order[b],
+// the rows sorted by descending length (counting sort over RL_ORDER_BINS
+// length buckets; rows within a bucket in any order).  The dispatcher starts
+// workgroups in index order and hands the next one to whichever CU frees up,
+// so the long rows start first and the short ones fill the tail (longest
+// processing time first).  In index order, 1024 rows of 8K-128K scores on
+// 512 resident workgroups finish about 1.6 times later than the balanced
+// schedule; longest first, within a few percent of it.
+constexpr int RL_ORDER_THREADS = 1024;
+constexpr int RL_ORDER_BINS = 1024;
+__global__ __launch_bounds__(RL_ORDER_THREADS) void k_ragged_order(RaggedArgs a)
+{
+    __shared__ uint32_t cnt[RL_ORDER_BINS];
+    __shared__ uint32_t s_wsum[RL_ORDER_THREADS / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t span = (uint64_t)a.pitch + 1u;
+    auto bin_of_row = [&](int r) {
+        const uint64_t L = row_length(a, r);
+        return (uint32_t)(((uint64_t)a.pitch - L) * RL_ORDER_BINS / span);  // 0 = longest
+    };
+    for (int i = tid; i < RL_ORDER_BINS; i += RL_ORDER_THREADS) cnt[i] = 0u;
+    __syncthreads();
+    for (int r = tid; r < a.M; r += RL_ORDER_THREADS) atomicAdd(&cnt[bin_of_row(r)], 1u);
+    __syncthreads();
+    // exclusive prefix over the bins (one bin per thread)
+    static_assert(RL_ORDER_BINS == RL_ORDER_THREADS, "one bin per thread");
+    const uint32_t v = cnt[tid];
+    const uint32_t incl = wave_incl_sum(v);
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    uint32_t off = 0;
+    for (int w = 0; w < wave; ++w) off += s_wsum[w];
+    cnt[tid] = off + incl - v;
+    __syncthreads();
+    for (int r = tid; r < a.M; r += RL_ORDER_THREADS) a.order[atomicAdd(&cnt[bin_of_row(r)], 1u)] = r;
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(RL_THREADS, 4) void k_ragged_rowlocal(RaggedArgs a)
 {
@@ -467,7 +505,7 @@ __global__ __launch_bounds__(RL_THREADS, 4) void k_ragged_rowlocal(RaggedArgs a)
     constexpr int U = RL_U;
     constexpr uint32_t CHUNK = (uint32_t)NT * U * 4;  // scores per chunk
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = blockIdx.x;
+    const int r = a.order[blockIdx.x];
     const uint32_t L = row_length(a, r);
     const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
     int32_t *out = a.out_idx + (size_t)r * a.k;
@@ -698,7 +736,8 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
         p.rlcap = kn.capacity > 0 && kn.capacity < STASH_CAP ? kn.capacity : STASH_CAP;
         p.P = 1;
         p.seg = pitch;
-        p.bytes = 256;  // no scratch: the route works on chip
+        p.off_order = 0;
+        p.bytes = align256((size_t)M * sizeof(int32_t));  // the row order; candidates stay on chip
         return p;
     }
     // Segmented route: about 512 workgroups (up to RAG_MAX_SPLITS segments
@@ -759,11 +798,15 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
     a.M = p.M; a.k = p.k; a.P = p.P; a.subcap = p.subcap; a.bandcap = p.bandcap;
     a.view_blocks = p.view_blocks; a.force = p.force;
     a.rlcap = p.rlcap;
+    a.order = nullptr;
     a.rho = p.rho; a.rho1 = p.rho1;
     const bool vec = (p.pitch % 4 == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0);
     hipError_t e;
     if (p.rowlocal) {
         StageTimer st(ST_RAG_ROWLOCAL, stream);
+        a.order = reinterpret_cast<int32_t *>(w + p.off_order);
+        e = launch_kernel(k_ragged_order, dim3(1), dim3(RL_ORDER_THREADS), stream, a);
+        if (e != hipSuccess) return e;
         return vec ? launch_kernel(k_ragged_rowlocal<true>, dim3(p.M), dim3(RL_THREADS), stream, a)
                    : launch_kernel(k_ragged_rowlocal<false>, dim3(p.M), dim3(RL_THREADS), stream, a);
     }
