@@ -79,3 +79,70 @@ def test_fused_graph_replays(itk, cfg):
         torch.cuda.synchronize()
         assert np.array_equal(np.sort(oi.cpu().numpy(), axis=1), eager[i][0]), f"replay {rep}: indices"
         assert np.array_equal(np.sort(osc.cpu().numpy(), axis=1), eager[i][1]), f"replay {rep}: scores"
+
+
+def test_history_sample_graph_replays(itk):
+    """The list builder and the gated fused call captured together (as a
+    prefill step would: build the next chunk's list, then run the chunk), six
+    replays on alternating inputs, each equal to the eager calls."""
+    pairs = [synth.prefill_chunk_pair(32, 64, 128, 9000, 256, seed=s) for s in (51, 52)]
+    T, k, N = 32, 256, 9000
+    kp = 3 * k
+    ts = [(itk.fused_tensors(p), itk.fused_tensors(c)) for p, c in pairs]
+    eager = []
+    for (Qp, K, _, Wp, kvp), (Q, _, _, W, kv) in ts:
+        prev_idx, _ = itk.indexer_topk_fused(Qp, K, Wp, kvp, k)
+        prior = itk.prior_from_topk(prev_idx, N, kp)
+        i, s = itk.indexer_topk_fused_prior(Q, K, W, kv, k, prior)
+        eager.append((prev_idx.clone(), prior.cpu().numpy(), np.sort(i.cpu().numpy(), axis=1)))
+    Kb = ts[0][0][1].clone()
+    Qb, Wb, kvb = ts[0][1][0].clone(), ts[0][1][3].clone(), ts[0][1][4].clone()
+    prev_b = eager[0][0].clone()
+    prior_b = torch.empty(kp, dtype=torch.int32, device="cuda")
+    pws = torch.empty(itk.prior_workspace_size(T, k, N, kp), dtype=torch.uint8, device="cuda")
+    oi = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    osc = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(itk.fused_prior_workspace_size(T, 64, 128, N, k, synth.BF16, synth.BF16, 0, kp),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        st = torch.cuda.current_stream()
+        itk.prior_from_topk(prev_b, N, kp, out=prior_b, workspace=pws, stream=st)
+        itk.indexer_topk_fused_prior(Qb, Kb, Wb, kvb, k, prior_b, out_idx=oi, out_score=osc, workspace=ws,
+                                     stream=st)
+
+    g = _capture(step)
+    for rep in range(6):
+        i = rep % 2
+        Kb.copy_(ts[i][0][1])
+        Qb.copy_(ts[i][1][0])
+        Wb.copy_(ts[i][1][3])
+        kvb.copy_(ts[i][1][4])
+        prev_b.copy_(eager[i][0])
+        oi.fill_(-7)
+        prior_b.fill_(-9)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(prior_b.cpu().numpy(), eager[i][1]), f"replay {rep}: list"
+        assert np.array_equal(np.sort(oi.cpu().numpy(), axis=1), eager[i][2]), f"replay {rep}: indices"
+
+
+def test_noalloc_graph_replays(itk):
+    """topk_ragged_noalloc captured and replayed: its static scratch carries
+    state only within a call."""
+    cases = [synth.gen_ragged(16, 8192, 300, lens=np.linspace(0, 8192, 16).astype(np.int32), seed=s,
+                              family="config2") for s in (61, 62)]
+    xs = [torch.from_numpy(c.scores).cuda() for c in cases]
+    rl = torch.from_numpy(cases[0].row_len).cuda()
+    k = cases[0].k
+    eager = [np.sort(itk.topk_ragged(x, rl, k).cpu().numpy(), axis=1) for x in xs]
+    buf = xs[0].clone()
+    out = torch.empty((16, k), dtype=torch.int32, device="cuda")
+    g = _capture(lambda: itk.topk_ragged_noalloc(buf, rl, k, out_idx=out, stream=torch.cuda.current_stream()))
+    for rep in range(6):
+        i = rep % 2
+        buf.copy_(xs[i])
+        out.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np.sort(out.cpu().numpy(), axis=1), eager[i]), f"replay {rep}"
