@@ -553,7 +553,8 @@ struct ScaleStage {
         const int64_t key = key0 + (int64_t)threadIdx.x;
         if (threadIdx.x < NSUB * TILE_KEYS) v = key < a.N ? a.k_scale[key] : 0.f;
     }
-    __device__ __forceinline__ void store(TileBuf<C> &tb, int buf) const
+    template <class TB>
+    __device__ __forceinline__ void store(TB &tb, int buf) const
     {
         if (threadIdx.x < NSUB * TILE_KEYS) tb.scale[buf][threadIdx.x] = v;
     }
@@ -675,7 +676,8 @@ struct KStage {
         }
     }
 
-    __device__ void store(TileBuf<C> &tb, int buf) const
+    template <class TB>
+    __device__ void store(TB &tb, int buf) const
     {
         const int tid = threadIdx.x;
         const int r = tid >> 3, part = tid & 7;
@@ -707,12 +709,13 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // lane l holding the score of key key0 + l (scaled by the per-key FP8 scale),
 // which the visitor must mask against the query's length.  Every thread of
 // the workgroup must call this.
-template <class C, int NSUB, class Visit>
-__device__ __forceinline__ void scan_tiles(const FusedArgs &a, TileBuf<C> &tb, const QFrags<C> &qf, int64_t first,
+template <class C, int NSUB, class TB, class Visit>
+__device__ __forceinline__ void scan_tiles(const FusedArgs &a, TB &tb, const QFrags<C> &qf, int64_t first,
                                            int64_t step, int nstages, int64_t key_end, bool active, uint32_t L,
                                            Visit &&visit)
 {
     static_assert(C::DMA || NSUB == 1, "FP8 staging moves one 64-key tile per stage");
+    static_assert(sizeof(tb.k[0]) >= NSUB * C::TILE_LDS, "stage buffer too small");
     const int lane = (int)lane_id();
     const int64_t kend = key_end < (int64_t)L ? key_end : (int64_t)L;
     KStage<C> ks;
@@ -885,10 +888,16 @@ __global__ __launch_bounds__(256) void k_prior_gather(FusedArgs a)
 }
 
 // -------------------------------------------- sample pass A: score range
-template <class C>
+// PRIOR: the history sample.  The scan then runs over the gathered entries
+// (their key rows stand in for K) in stages of the main scan's size (the
+// entries of a split are contiguous tiles), and entry e is usable for the row
+// when its key is below the row's length.  A separate instantiation, so that
+// the strided view keeps its own register allocation.
+template <class C, bool PRIOR>
 __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
 {
-    __shared__ TileBuf<C> tb;
+    constexpr int NS = PRIOR ? C::NSUB : 1;  // 64-key tiles per stage
+    __shared__ TileBuf<C, NS> tb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int g, p;
     map_group_split(blockIdx.x, a.G, a.Ps, g, p);
@@ -903,20 +912,16 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
         if (lane == 0) {
             a.tail[t] = 0u;
             a.rflag[t] = 0u;
-            if (a.pidx) a.pcount[t] = 0u;
+            if (PRIOR) a.pcount[t] = 0u;
         }
     }
-    // History sample: the scan runs over the gathered entries (their key rows
-    // stand in for K), and entry e is usable for the row when its key is
-    // below the row's length.
-    const bool prior = a.pidx != nullptr;
     FusedArgs sa = a;
-    if (prior) {
+    if (PRIOR) {
         sa.K = a.Kp;
         sa.k_scale = a.kp_scale;
         sa.N = a.np;
     }
-    const uint32_t maxL = prior ? (uint32_t)a.np : group_max_len(a, g);
+    const uint32_t maxL = PRIOR ? (uint32_t)a.np : group_max_len(a, g);
     const SampleIter it = sample_iter(a, g, p, maxL);
     QFrags<C> qf;
     if (active) qf.load(a, t);
@@ -926,9 +931,11 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
     // that pass B bins them without scoring the view again.
     const int64_t phase = g % a.sample_tiles;
     float *srow = a.samp ? a.samp + (size_t)(active ? t : 0) * a.samp_cap : nullptr;
-    const uint32_t Lscan = prior ? (uint32_t)a.np : L;
-    scan_tiles<C, 1>(sa, tb, qf, it.first_key, it.stride_keys, it.ntiles, it.end, active, Lscan, [&](int64_t key0, float s) {
-        const bool valid = prior ? a.pidx[key0 + lane] < (int32_t)L : key0 + lane < (int64_t)L;
+    const uint32_t Lscan = PRIOR ? (uint32_t)a.np : L;
+    const int64_t step = PRIOR ? (int64_t)NS * TILE_KEYS : it.stride_keys;
+    const int nst = PRIOR ? (it.ntiles + NS - 1) / NS : it.ntiles;
+    scan_tiles<C, NS>(sa, tb, qf, it.first_key, step, nst, it.end, active, Lscan, [&](int64_t key0, float s) {
+        const bool valid = PRIOR ? a.pidx[key0 + lane] < (int32_t)L : key0 + lane < (int64_t)L;
         if (valid) {
             mn = fminf(mn, s);
             mx = fmaxf(mx, s);
@@ -1612,7 +1619,8 @@ hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t 
             e = launch_kernel(k_prior_gather<C>, dim3((unsigned)((threads + 255) / 256)), dim3(256), stream, a);
         }
         if (e == hipSuccess)
-            e = launch_kernel(k_fused_minmax<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a);
+            e = a.pidx ? launch_kernel(k_fused_minmax<C, true>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a)
+                       : launch_kernel(k_fused_minmax<C, false>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a);
     }
     if (e != hipSuccess) return e;
     {
