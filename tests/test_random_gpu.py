@@ -79,3 +79,26 @@ def test_random_fused(itk, i):
         return
     torch.cuda.synchronize()
     check_fused_rows(case, range(case.T), idx.cpu().numpy(), sc.cpu().numpy())
+
+
+@pytest.mark.parametrize("i", range(0, N_CASES, 2))
+def test_random_fused_history_sample(itk, i):
+    """The same random cases gated by a random key list (random length, keys
+    inside and outside [0, N), repeats): the result is the exact Top-k
+    whatever the list; the single-head path rejects a list."""
+    case, fp8_score = _fused_case(i)
+    if fp8_score:
+        case.flags |= itk.FLAG_FP8_SCORE
+    rng = np.random.default_rng(500 + i)
+    n_prior = int(rng.integers(1, 3 * max(case.k, 1) + 64))
+    prior = rng.integers(-5, case.N + 5, size=n_prior).astype(np.int32)
+    Q, K, S, W, kv = itk.fused_tensors(case)
+    try:
+        idx, sc = itk.indexer_topk_fused_prior(Q, K, W, kv, case.k, torch.from_numpy(prior).cuda(), k_scale=S,
+                                               flags=case.flags)
+    except itk.ITKError as e:
+        # the single-head path takes no list; FP8 scoring needs two heads
+        assert e.status == 2 and case.H == 1, str(e)
+        return
+    torch.cuda.synchronize()
+    check_fused_rows(case, range(case.T), idx.cpu().numpy(), sc.cpu().numpy())
