@@ -168,6 +168,7 @@ struct FusedArgs {
     float *samp;       // [T][samp_cap] scores of the sampled view (both paths)
     uint32_t *hist_r;  // [T][NBINS] full-row histogram of rows under recovery (head rows)
     uint32_t *rflag;   // [T] 1 when the row went through the grid-wide recovery (head rows)
+    uint32_t *gpub;    // [T] gate bin published across the key splits of a row (head rows)
     // single-head (query-column) path
     float *gate;       // [T] admission gate (score space)
     uint32_t *qcnt;    // [T][P] candidates per (query, key split); may exceed capS
@@ -709,10 +710,18 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // lane l holding the score of key key0 + l (scaled by the per-key FP8 scale),
 // which the visitor must mask against the query's length.  Every thread of
 // the workgroup must call this.
-template <class C, int NSUB, class TB, class Visit>
+// Per-stage hook of scan_tiles: issue() runs just before the wait for the
+// next stage's copy (a load it issues completes with that wait), use() just
+// after the stage barrier.
+struct NoStageHook {
+    __device__ __forceinline__ void issue() {}
+    __device__ __forceinline__ void use() {}
+};
+
+template <class C, int NSUB, class TB, class Visit, class Hook = NoStageHook>
 __device__ __forceinline__ void scan_tiles(const FusedArgs &a, TB &tb, const QFrags<C> &qf, int64_t first,
                                            int64_t step, int nstages, int64_t key_end, bool active, uint32_t L,
-                                           Visit &&visit)
+                                           Visit &&visit, Hook &&hook = Hook{})
 {
     static_assert(C::DMA || NSUB == 1, "FP8 staging moves one 64-key tile per stage");
     static_assert(sizeof(tb.k[0]) >= NSUB * C::TILE_LDS, "stage buffer too small");
@@ -783,10 +792,12 @@ __device__ __forceinline__ void scan_tiles(const FusedArgs &a, TB &tb, const QFr
         }
         if (st + 1 < nstages) {
             if constexpr (!C::DMA) ks.store(tb, buf ^ 1);
+            hook.issue();
             wait_vmem_all();
             if constexpr (DSCALE) ss.store(tb, buf ^ 1);
         }
         __syncthreads();
+        if (st + 1 < nstages) hook.use();
     }
     if (pend >= 0) {
         const float p1 = reduce_block<C>(accB, qf.w);
@@ -912,6 +923,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_minmax(FusedArgs a)
         if (lane == 0) {
             a.tail[t] = 0u;
             a.rflag[t] = 0u;
+            a.gpub[t] = 0u;
             if (PRIOR) a.pcount[t] = 0u;
         }
     }
@@ -1114,6 +1126,40 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
         }
         if ((uint32_t)lane < n && slot + lane < cap) cand[slot + lane] = stage[lane];
     };
+    // Moves the gate up to bin nb (<= NBINS - 1), keeping the counts.
+    auto raise_to = [&](int nb) __attribute__((always_inline)) {
+        while (gate_bin < nb) {
+            inrange -= at_gate;
+            ++gate_bin;
+            at_gate = whist[gate_bin];
+        }
+        gate_f = (float)gate_bin;
+    };
+    // Under key splits each split refreshes its gate from its own admitted
+    // keys; a split whose own keys put the gate above a bin proves that every
+    // key of the row's Top-k lies above it (LiteTopK Sec. 3.2), so the bin is
+    // published to the row's word (atomic max) and the other splits of the
+    // row read it once per stage, with the stage's copy, and move up to it.
+    const bool publish = !own_row && active && refresh;
+    struct PubHook {
+        const FusedArgs &a;
+        int t;
+        bool on;
+        uint32_t v;
+        decltype(raise_to) &raise;
+        const int &cur;
+        __device__ __forceinline__ void issue()
+        {
+            if (on) v = a.gpub[t];
+        }
+        __device__ __forceinline__ void use()
+        {
+            if (on) {
+                const int pub = (int)__builtin_amdgcn_readfirstlane(v);
+                if (pub > cur) raise(pub < NBINS - 1 ? pub : NBINS - 1);
+            }
+        }
+    } hook{a, t, publish, 0u, raise_to, gate_bin};
 
     scan_tiles<C, C::NSUB>(a, tb, qf, k_lo, C::STAGE_KEYS, nstages, k_hi, active, L, [&](int64_t key0, float s) {
         const int64_t key = key0 + lane;
@@ -1147,9 +1193,10 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_main(FusedArgs a)
                     at_gate = whist[gate_bin];
                 } while (inrange - at_gate >= kq && gate_bin < NBINS - 1);
                 gate_f = (float)gate_bin;
+                if (publish && lane == 0) atomicMax(&a.gpub[t], (uint32_t)gate_bin);
             }
         }
-    });
+    }, hook);
     if (active && stage_n) flush(stage_n);
     if (active && own_row && lane == 0) a.tail[t] = tail_reg;
 }

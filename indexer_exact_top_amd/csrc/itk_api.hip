@@ -230,6 +230,7 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
     p.off_samp = off; off = align256(off + (size_t)T * p.samp_cap * sizeof(float));
     p.off_hist_r = off; off = align256(off + (size_t)T * NBINS * sizeof(uint32_t));
     p.off_rflag = off; off = align256(off + (size_t)T * sizeof(uint32_t));
+    p.off_gpub = off; off = align256(off + (size_t)T * sizeof(uint32_t));
     if (n_prior > 0) {
         p.off_pidx = off; off = align256(off + (size_t)p.np * sizeof(int32_t));
         p.off_kp = off; off = align256(off + (size_t)p.np * p.rowb);
@@ -263,6 +264,7 @@ hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const 
     a.samp = p.samp_cap > 0 ? reinterpret_cast<float *>(w + p.off_samp) : nullptr;
     a.hist_r = p.qrow ? nullptr : reinterpret_cast<uint32_t *>(w + p.off_hist_r);
     a.rflag = p.qrow ? nullptr : reinterpret_cast<uint32_t *>(w + p.off_rflag);
+    a.gpub = p.qrow ? nullptr : reinterpret_cast<uint32_t *>(w + p.off_gpub);
     a.samp_cap = p.samp_cap;
     a.gate = nullptr; a.qcnt = nullptr; a.capS = 0;
     a.prior = nullptr; a.pidx = nullptr; a.Kp = nullptr; a.kp_scale = nullptr; a.pcount = nullptr;

@@ -150,7 +150,7 @@ struct FusedPlan {
     int32_t capS = 0;        // single head: candidates per (query, key split)
     int64_t samp_cap = 0;    // single head: stored view scores per query
     size_t off_param = 0, off_mm = 0, off_hist = 0, off_tail = 0, off_gate = 0, off_cand = 0;
-    size_t off_hist_r = 0, off_rflag = 0;
+    size_t off_hist_r = 0, off_rflag = 0, off_gpub = 0;
     size_t off_samp = 0, off_qcnt = 0, bytes = 0;
     // history sample (head rows only): listed entries, padded entries, key row bytes
     int32_t n_prior = 0, rowb = 0;
