@@ -75,8 +75,9 @@ constexpr int FIN_MANY_ROWS = 256;
 // RAG_RL_MAX_PITCH scores and secondary counts rho1 * k of at most
 // RAG_RL_MAX_CAND (the on-chip stash holds STASH_CAP).  One CU streams a row
 // at a few tens of GB/s, so the route needs enough rows to occupy the chip:
-// measured on rows of 8K-128K scores (k = 2048), 1024 rows take 92 us
-// row-local against 106 us segmented, 64 rows 39 us against 22.5 us.
+// measured on rows of 8K-128K scores (k = 2048), 1024 rows take 76-78 us
+// row-local (rows longest first) against 106 us segmented, 64 rows 39 us
+// against 22.5 us.
 #ifndef RL_THREADS_DEF
 #define RL_THREADS_DEF 512
 #endif
