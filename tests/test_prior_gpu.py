@@ -26,8 +26,11 @@ def _reset(itk):
     itk.reset_plan_opts()
 
 
+# N = 2^20 spans 32 key ranges of the counting step, so its entries are
+# counted one global atomic each; the others count through LDS per range.
 @pytest.mark.parametrize("T,k,N,kp,seed", [(7, 20, 300, 50, 1), (64, 256, 4096, 768, 2), (3, 5, 40, 64, 3),
-                                           (0, 8, 100, 10, 4), (300, 2048, 133120, 6144, 5)])
+                                           (0, 8, 100, 10, 4), (300, 2048, 133120, 6144, 5),
+                                           (64, 512, 1 << 20, 1536, 6)])
 def test_prior_from_topk_matches_oracle(itk, T, k, N, kp, seed):
     rng = np.random.default_rng(seed)
     # skewed key popularity, -1 padding and entries outside [0, N)
