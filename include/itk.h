@@ -79,6 +79,11 @@ typedef enum {
  *            topk_ragged_workspace_size(M, row_pitch, k) bytes, 256-byte
  *            aligned; contents need no initialisation and are meaningless
  *            between calls.  Concurrent calls must not share a workspace.
+ *   Empty problems: M == 0 or k == 0 returns ITK_OK with nothing enqueued
+ *   and no pointer read; row_pitch == 0 leaves every row empty, so only the
+ *   -1 padding of out_idx is written (scores, row_len and the workspace are
+ *   not read; the workspace size is 0).  Negative sizes are
+ *   ITK_ERR_INVALID_ARG.
  *
  * Method: a block-strided view of the row proposes a coarse boundary, one
  * complete-row pass certifies it and collects the admitted candidates, and an
@@ -146,6 +151,12 @@ itk_status topk_ragged_noalloc(const float *scores, int64_t row_pitch, const int
  *   holds every query's sampled-view scores (at most about 32768 per query).
  *   Results follow the same contract on either path.
  *   workspace: as for topk_ragged.
+ *   Empty problems: once H, D, the dtypes and the flags pass the checks of
+ *   a non-empty call, T == 0 or k == 0 returns ITK_OK with nothing enqueued
+ *   and no pointer read; N == 0 leaves every row empty, so only the padding
+ *   of out_idx and out_score is written (Q, K, k_scale, W, kv_len and the
+ *   workspace are not read; the workspace size is 0).  Negative sizes are
+ *   ITK_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------ */
 size_t indexer_topk_fused_workspace_size(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k,
                                          itk_dtype q_t, itk_dtype k_t, uint32_t flags);

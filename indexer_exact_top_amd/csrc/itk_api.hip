@@ -294,12 +294,6 @@ hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const 
     return fn(p, a, stream);
 }
 
-}  // namespace itk
-
-using namespace itk;
-
-extern "C" {
-
 // Name of the HIP error behind the last ITK_ERR_HIP of this thread.
 static thread_local hipError_t g_last_hip = hipSuccess;
 
@@ -309,6 +303,65 @@ static itk_status hip_status(hipError_t e)
     g_last_hip = e;
     return ITK_ERR_HIP;
 }
+
+// The padding of rows with no valid key: -1 indices and -inf scores (when
+// `score` is given).
+__global__ __launch_bounds__(256) void k_fill_pad(int32_t *idx, float *score, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        idx[i] = -1;
+        if (score) score[i] = -__builtin_inff();
+    }
+}
+
+static hipError_t fill_pad(int32_t *idx, float *score, int64_t n, hipStream_t stream)
+{
+    const int64_t blocks = (n + 255) / 256;
+    return launch_kernel(k_fill_pad, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), stream, idx, score,
+                         n);
+}
+
+bool ragged_trivial(int32_t M, int64_t row_pitch, int32_t k, int32_t *out_idx, hipStream_t stream, itk_status *st)
+{
+    if (M > 0 && k > 0 && row_pitch > 0) return false;
+    if (M < 0 || k < 0 || row_pitch < 0) {
+        *st = ITK_ERR_INVALID_ARG;
+    } else if (M == 0 || k == 0) {
+        *st = ITK_OK;
+    } else {
+        *st = out_idx ? hip_status(fill_pad(out_idx, nullptr, (int64_t)M * k, stream)) : ITK_ERR_INVALID_ARG;
+    }
+    return true;
+}
+
+// Fused calls with nothing to score.  Returns true when the call is
+// complete, with its status in *st.  The shape and dtypes are checked as for
+// a non-empty call; then no queries or k == 0 enqueue nothing, and no keys
+// (N == 0) leave every row empty, so only the padding is written.
+static bool fused_trivial(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk_dtype q_t, itk_dtype k_t,
+                          uint32_t flags, int32_t n_prior, int32_t *out_idx, float *out_score, hipStream_t stream,
+                          itk_status *st)
+{
+    if (T > 0 && k > 0 && N > 0) return false;
+    if (T < 0 || k < 0 || N < 0) {
+        *st = ITK_ERR_INVALID_ARG;
+        return true;
+    }
+    FusedPlan p;
+    *st = plan_fused(T > 0 ? T : 1, H, D, N > 0 ? N : 1, k > 0 ? k : 1, q_t, k_t, flags, &p, n_prior);
+    if (*st != ITK_OK || T == 0 || k == 0) return true;
+    *st = (out_idx && out_score) ? hip_status(fill_pad(out_idx, out_score, (int64_t)T * k, stream))
+                                 : ITK_ERR_INVALID_ARG;
+    return true;
+}
+
+}  // namespace itk
+
+using namespace itk;
+
+extern "C" {
+
 
 const char *itk_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
@@ -334,8 +387,9 @@ size_t topk_ragged_workspace_size(int32_t M, int64_t row_pitch, int32_t k)
 itk_status topk_ragged(const float *scores, int64_t row_pitch, const int32_t *row_len, int32_t M, int32_t k,
                        int32_t *out_idx, void *workspace, size_t workspace_bytes, void *stream)
 {
+    itk_status st;
+    if (ragged_trivial(M, row_pitch, k, out_idx, static_cast<hipStream_t>(stream), &st)) return st;
     if (!scores || !row_len || !out_idx) return ITK_ERR_INVALID_ARG;
-    if (M <= 0 || k <= 0 || row_pitch <= 0) return ITK_ERR_INVALID_ARG;
     if (row_pitch > (int64_t)0x7FFFFFFF) return ITK_ERR_UNSUPPORTED;
     const RaggedPlan p = plan_ragged(M, row_pitch, k);
     if (!workspace || workspace_bytes < p.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -357,11 +411,14 @@ itk_status indexer_topk_fused(const void *Q, itk_dtype q_t, const void *K, itk_d
                               int32_t k, uint32_t flags, int32_t *out_idx, float *out_score, void *workspace,
                               size_t workspace_bytes, void *stream)
 {
+    itk_status st;
+    if (fused_trivial(T, H, D, N, k, q_t, k_t, flags, 0, out_idx, out_score, static_cast<hipStream_t>(stream), &st))
+        return st;
     if (!Q || !K || !W || !kv_len || !out_idx || !out_score) return ITK_ERR_INVALID_ARG;
     if ((k_t == ITK_FP8_E4M3) != (k_scale != nullptr)) return ITK_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(Q) & 15u) || (reinterpret_cast<uintptr_t>(K) & 15u)) return ITK_ERR_INVALID_ARG;
     FusedPlan p;
-    const itk_status st = plan_fused(T, H, D, N, k, q_t, k_t, flags, &p);
+    st = plan_fused(T, H, D, N, k, q_t, k_t, flags, &p);
     if (st != ITK_OK) return st;
     if (!workspace || workspace_bytes < p.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return ITK_ERR_WORKSPACE;
@@ -384,12 +441,17 @@ itk_status indexer_topk_fused_prior(const void *Q, itk_dtype q_t, const void *K,
                                     const int32_t *prior_idx, int32_t n_prior, int32_t *out_idx, float *out_score,
                                     void *workspace, size_t workspace_bytes, void *stream)
 {
+    itk_status st;
+    if (n_prior < 0) return ITK_ERR_INVALID_ARG;
+    if (fused_trivial(T, H, D, N, k, q_t, k_t, flags, n_prior, out_idx, out_score, static_cast<hipStream_t>(stream),
+                      &st))
+        return st;
     if (!Q || !K || !W || !kv_len || !out_idx || !out_score) return ITK_ERR_INVALID_ARG;
     if ((k_t == ITK_FP8_E4M3) != (k_scale != nullptr)) return ITK_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(Q) & 15u) || (reinterpret_cast<uintptr_t>(K) & 15u)) return ITK_ERR_INVALID_ARG;
-    if (n_prior < 0 || (n_prior > 0 && !prior_idx)) return ITK_ERR_INVALID_ARG;
+    if (n_prior > 0 && !prior_idx) return ITK_ERR_INVALID_ARG;
     FusedPlan p;
-    const itk_status st = plan_fused(T, H, D, N, k, q_t, k_t, flags, &p, n_prior);
+    st = plan_fused(T, H, D, N, k, q_t, k_t, flags, &p, n_prior);
     if (st != ITK_OK) return st;
     if (!workspace || workspace_bytes < p.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return ITK_ERR_WORKSPACE;

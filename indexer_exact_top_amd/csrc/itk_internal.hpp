@@ -109,6 +109,12 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k);
 hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t *row_len,
                          int32_t *out_idx, void *ws, hipStream_t stream);
 
+// Ragged calls with nothing to refine.  Returns true when the call is
+// complete, with its status in *st: a negative size is invalid; no rows or
+// k == 0 enqueue nothing; rows of pitch 0 are all empty, so only the -1
+// padding of out_idx is written.
+bool ragged_trivial(int32_t M, int64_t row_pitch, int32_t k, int32_t *out_idx, hipStream_t stream, itk_status *st);
+
 // ---------------------------------------------------------------- fused
 constexpr int FUSED_WAVES = 8;                  // queries per workgroup
 constexpr int FUSED_THREADS = FUSED_WAVES * 64;

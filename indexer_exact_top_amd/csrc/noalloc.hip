@@ -48,8 +48,9 @@ extern "C" itk_status topk_ragged_noalloc(const float *scores, int64_t row_pitch
                                           int32_t k, int32_t *out_idx, void *stream)
 {
     using namespace itk;
+    itk_status st;
+    if (ragged_trivial(M, row_pitch, k, out_idx, static_cast<hipStream_t>(stream), &st)) return st;
     if (!scores || !row_len || !out_idx) return ITK_ERR_INVALID_ARG;
-    if (M <= 0 || k <= 0 || row_pitch <= 0) return ITK_ERR_INVALID_ARG;
     if (row_pitch > (int64_t)0x7FFFFFFF) return ITK_ERR_UNSUPPORTED;
     const RaggedPlan p = plan_ragged(M, row_pitch, k);
     if (p.bytes > (size_t)ITK_RAGGED_NOALLOC_SCRATCH_BYTES) return ITK_ERR_SCRATCH_LIMIT;

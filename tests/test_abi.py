@@ -41,9 +41,19 @@ def test_ragged_validation():
     ws = lib.topk_ragged_workspace_size(64, 131072, 2048)
     assert ws > 0
     assert lib.topk_ragged(None, 128, FAKE, 4, 8, FAKE, FAKE, ws, None) == 1
-    assert lib.topk_ragged(FAKE, 128, FAKE, 0, 8, FAKE, FAKE, ws, None) == 1
-    assert lib.topk_ragged(FAKE, 128, FAKE, 4, 0, FAKE, FAKE, ws, None) == 1
-    assert lib.topk_ragged(FAKE, 0, FAKE, 4, 8, FAKE, FAKE, ws, None) == 1
+    # negative sizes are invalid; no rows or k == 0 is a complete call that
+    # enqueues nothing (no pointer is read, so none is needed)
+    assert lib.topk_ragged(FAKE, 128, FAKE, -1, 8, FAKE, FAKE, ws, None) == 1
+    assert lib.topk_ragged(FAKE, 128, FAKE, 4, -1, FAKE, FAKE, ws, None) == 1
+    assert lib.topk_ragged(FAKE, -1, FAKE, 4, 8, FAKE, FAKE, ws, None) == 1
+    assert lib.topk_ragged(None, 128, None, 0, 8, None, None, 0, None) == 0
+    assert lib.topk_ragged(None, 128, None, 4, 0, None, None, 0, None) == 0
+    assert lib.topk_ragged_noalloc(None, 128, None, 0, 8, None, None) == 0
+    assert lib.topk_ragged_noalloc(None, 128, None, 4, 0, None, None) == 0
+    assert lib.topk_ragged_workspace_size(0, 128, 8) == 0
+    # rows of pitch 0 are empty: only the padding is written, so out_idx is needed
+    assert lib.topk_ragged(None, 0, None, 4, 8, None, None, 0, None) == 1
+    assert lib.topk_ragged_noalloc(None, 0, None, 4, 8, None, None) == 1
     assert lib.topk_ragged(FAKE, 1 << 31, FAKE, 4, 8, FAKE, FAKE, ws, None) == 2
     need = lib.topk_ragged_workspace_size(4, 128, 8)
     assert lib.topk_ragged(FAKE, 128, FAKE, 4, 8, FAKE, None, need, None) == 3
@@ -64,8 +74,17 @@ def test_fused_validation():
     assert call(args(Q=None)) == 1
     assert call(args(kt=FP8)) == 1                  # fp8 keys need a scale
     assert call(args(S=FAKE)) == 1                  # a scale only with fp8 keys
-    assert call(args(T=0)) == 1
-    assert call(args(k=0)) == 1
+    # negative sizes are invalid; no queries or k == 0 is a complete call that
+    # enqueues nothing, once the shape and dtypes pass the same checks
+    assert call(args(T=-1)) == 1 and call(args(k=-1)) == 1 and call(args(N=-1)) == 1
+    assert call(args(T=0, Q=None, K=None, W=None, kv=None, oi=None, os=None, ws=None, wsb=0)) == 0
+    assert call(args(k=0, Q=None, K=None, W=None, kv=None, oi=None, os=None, ws=None, wsb=0)) == 0
+    assert call(args(T=0, H=65)) == 2
+    assert call(args(k=0, D=96)) == 2
+    assert call(args(T=0, flags=1, H=2)) == 1
+    # no keys: every row is empty, only the padding is written (outputs needed)
+    assert call(args(N=0, oi=None)) == 1
+    assert lib.indexer_topk_fused_workspace_size(0, 8, 64, 1000, 16, BF, BF, 0) == 0
     assert call(args(H=65)) == 2
     assert call(args(D=96)) == 2
     assert call(args(H=40, D=256)) == 2             # two head blocks need D <= 128
@@ -146,6 +165,8 @@ def test_history_sample_validation():
         FAKE, qt, FAKE, qt, None, FAKE, FAKE, 4, H, D, 1000, 16, fl, pr, n, FAKE, FAKE, FAKE, 1 << 40, None)
     assert call(-1) == 1
     assert call(5, pr=None) == 1
+    assert lib.indexer_topk_fused_prior(None, BF, None, BF, None, None, None, 0, 64, 128, 1000, 16, 0, None, 5,
+                                        None, None, None, 0, None) == 0     # no queries
     assert call((1 << 16) + 1) == 2
     assert call(64, H=1, D=256, qt=F16, fl=1) == 2
     # the list builder
