@@ -122,6 +122,26 @@ def _check(status: int, what: str):
         raise ITKError(status, what)
 
 
+def _need(t, name: str, dtypes, shape=None, device=None):
+    """Checks that ``t`` is a contiguous device tensor of one of ``dtypes``
+    (and of ``shape`` / on ``device`` when given): the kernels read every
+    buffer as a dense row-major array of that element type."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's tensors are on {device}")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major without gaps)")
+
+
 def _dtype_code(t) -> int:
     import torch
     m = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.float8_e4m3fn: FP8_E4M3}
@@ -138,14 +158,18 @@ def topk_ragged_workspace_size(M: int, pitch: int, k: int) -> int:
 def topk_ragged(scores, row_len, k: int, out_idx=None, workspace=None, stream=None):
     """Exact Top-k of each ragged fp32 row; returns int32 [M, k] (set order, -1 pad)."""
     import torch
-    assert scores.is_cuda and scores.dtype == torch.float32 and scores.dim() == 2
-    assert scores.stride(1) == 1
-    M, pitch = scores.shape[0], scores.stride(0)
+    _need(scores, "scores", torch.float32)
+    if scores.dim() != 2:
+        raise ValueError(f"scores must be [M, pitch], got shape {tuple(scores.shape)}")
+    M, pitch = scores.shape
+    dev = scores.device
+    _need(row_len, "row_len", torch.int32, (M,), dev)
     if out_idx is None:
-        out_idx = torch.empty((M, k), dtype=torch.int32, device=scores.device)
+        out_idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    _need(out_idx, "out_idx", torch.int32, (M, k), dev)
     if workspace is None:
-        workspace = torch.empty(max(1, topk_ragged_workspace_size(M, pitch, k)), dtype=torch.uint8,
-                                device=scores.device)
+        workspace = torch.empty(max(1, topk_ragged_workspace_size(M, pitch, k)), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
     st = lib().topk_ragged(_ptr(scores), pitch, _ptr(row_len), M, k, _ptr(out_idx), _ptr(workspace),
                            workspace.numel(), _stream(stream))
     _check(st, "topk_ragged")
@@ -156,9 +180,12 @@ def topk_ragged_noalloc(scores, row_len, k: int, out_idx, stream=None):
     """topk_ragged with the library's static scratch (no workspace, nothing
     allocated by the call; ``out_idx`` [M, k] int32 must be given)."""
     import torch
-    assert scores.is_cuda and scores.dtype == torch.float32 and scores.dim() == 2
-    assert scores.stride(1) == 1
-    M, pitch = scores.shape[0], scores.stride(0)
+    _need(scores, "scores", torch.float32)
+    if scores.dim() != 2:
+        raise ValueError(f"scores must be [M, pitch], got shape {tuple(scores.shape)}")
+    M, pitch = scores.shape
+    _need(row_len, "row_len", torch.int32, (M,), scores.device)
+    _need(out_idx, "out_idx", torch.int32, (M, k), scores.device)
     st = lib().topk_ragged_noalloc(_ptr(scores), pitch, _ptr(row_len), M, k, _ptr(out_idx), _stream(stream))
     _check(st, "topk_ragged_noalloc")
     return out_idx
@@ -169,22 +196,48 @@ def fused_workspace_size(T, H, D, N, k, q_t, k_t, flags=0) -> int:
     return int(lib().indexer_topk_fused_workspace_size(T, H, D, N, k, q_t, k_t, flags))
 
 
+def _fused_inputs(Q, K, W, kv_len, k_scale):
+    """Validates the fused inputs; returns (T, H, D, N, q_t, k_t)."""
+    import torch
+    _need(Q, "Q", (torch.bfloat16, torch.float16, torch.float32))
+    if Q.dim() != 3:
+        raise ValueError(f"Q must be [T, H, D], got shape {tuple(Q.shape)}")
+    T, H, D = Q.shape
+    dev = Q.device
+    _need(K, "K", (torch.bfloat16, torch.float16, torch.float32, torch.float8_e4m3fn), None, dev)
+    if K.dim() != 2 or K.shape[1] != D:
+        raise ValueError(f"K must be [N, {D}], got shape {tuple(K.shape)}")
+    N = K.shape[0]
+    _need(W, "W", torch.float32, (T, H), dev)
+    _need(kv_len, "kv_len", torch.int32, (T,), dev)
+    if k_scale is not None:
+        _need(k_scale, "k_scale", torch.float32, (N,), dev)
+    return T, H, D, N, _dtype_code(Q), _dtype_code(K)
+
+
+def _fused_outputs(T, k, dev, out_idx, out_score):
+    import torch
+    if out_idx is None:
+        out_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if out_score is None:
+        out_score = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(out_idx, "out_idx", torch.int32, (T, k), dev)
+    _need(out_score, "out_score", torch.float32, (T, k), dev)
+    return out_idx, out_score
+
+
 def indexer_topk_fused(Q, K, W, kv_len, k: int, k_scale=None, flags: int = 0, out_idx=None, out_score=None,
                        workspace=None, stream=None):
     """Fused indexer score + exact Top-k.  Q [T,H,D], K [N,D] (bf16/f16/f32 or
     float8_e4m3fn with k_scale [N]), W [T,H] fp32, kv_len [T] int32.
     Returns (out_idx int32 [T,k], out_score fp32 [T,k])."""
     import torch
-    T, H, D = Q.shape
-    N = K.shape[0]
-    q_t, k_t = _dtype_code(Q), _dtype_code(K)
-    if out_idx is None:
-        out_idx = torch.empty((T, k), dtype=torch.int32, device=Q.device)
-    if out_score is None:
-        out_score = torch.empty((T, k), dtype=torch.float32, device=Q.device)
+    T, H, D, N, q_t, k_t = _fused_inputs(Q, K, W, kv_len, k_scale)
+    out_idx, out_score = _fused_outputs(T, k, Q.device, out_idx, out_score)
     if workspace is None:
         workspace = torch.empty(max(1, fused_workspace_size(T, H, D, N, k, q_t, k_t, flags)),
                                 dtype=torch.uint8, device=Q.device)
+    _need(workspace, "workspace", torch.uint8, None, Q.device)
     st = lib().indexer_topk_fused(_ptr(Q), q_t, _ptr(K), k_t, _ptr(k_scale), _ptr(W), _ptr(kv_len), T, H, D, N,
                                   k, flags, _ptr(out_idx), _ptr(out_score), _ptr(workspace), workspace.numel(),
                                   _stream(stream))
@@ -201,19 +254,15 @@ def indexer_topk_fused_prior(Q, K, W, kv_len, k: int, prior, k_scale=None, flags
     """indexer_topk_fused with a history sample: ``prior`` is an int32 device
     tensor of key indices (the previous chunk's most frequent keys)."""
     import torch
-    T, H, D = Q.shape
-    N = K.shape[0]
-    q_t, k_t = _dtype_code(Q), _dtype_code(K)
+    T, H, D, N, q_t, k_t = _fused_inputs(Q, K, W, kv_len, k_scale)
     n_prior = int(prior.numel()) if prior is not None else 0
-    if prior is not None and (prior.dtype != torch.int32 or not prior.is_contiguous()):
-        raise TypeError("prior must be a contiguous int32 tensor")
-    if out_idx is None:
-        out_idx = torch.empty((T, k), dtype=torch.int32, device=Q.device)
-    if out_score is None:
-        out_score = torch.empty((T, k), dtype=torch.float32, device=Q.device)
+    if prior is not None:
+        _need(prior, "prior", torch.int32, (n_prior,), Q.device)
+    out_idx, out_score = _fused_outputs(T, k, Q.device, out_idx, out_score)
     if workspace is None:
         workspace = torch.empty(max(1, fused_prior_workspace_size(T, H, D, N, k, q_t, k_t, flags, n_prior)),
                                 dtype=torch.uint8, device=Q.device)
+    _need(workspace, "workspace", torch.uint8, None, Q.device)
     st = lib().indexer_topk_fused_prior(_ptr(Q), q_t, _ptr(K), k_t, _ptr(k_scale), _ptr(W), _ptr(kv_len), T, H, D,
                                         N, k, flags, _ptr(prior), n_prior, _ptr(out_idx), _ptr(out_score),
                                         _ptr(workspace), workspace.numel(), _stream(stream))
@@ -229,14 +278,17 @@ def prior_from_topk(prev_idx, N: int, k_prime: int, out=None, workspace=None, st
     """The k_prime most frequent keys of the previous chunk's lists
     ``prev_idx`` (int32 [T_prev, k], device); returns int32 [k_prime]."""
     import torch
-    if prev_idx.dtype != torch.int32 or prev_idx.dim() != 2 or not prev_idx.is_contiguous():
-        raise TypeError("prev_idx must be a contiguous int32 [T_prev, k] tensor")
+    _need(prev_idx, "prev_idx", torch.int32)
+    if prev_idx.dim() != 2:
+        raise ValueError(f"prev_idx must be [T_prev, k], got shape {tuple(prev_idx.shape)}")
     T_prev, k = prev_idx.shape
     if out is None:
         out = torch.empty(k_prime, dtype=torch.int32, device=prev_idx.device)
+    _need(out, "out", torch.int32, (k_prime,), prev_idx.device)
     if workspace is None:
         workspace = torch.empty(max(1, prior_workspace_size(T_prev, k, N, k_prime)), dtype=torch.uint8,
                                 device=prev_idx.device)
+    _need(workspace, "workspace", torch.uint8, None, prev_idx.device)
     st = lib().indexer_prior_from_topk(_ptr(prev_idx), T_prev, k, N, k_prime, _ptr(out), _ptr(workspace),
                                        workspace.numel(), _stream(stream))
     _check(st, "indexer_prior_from_topk")
@@ -275,10 +327,16 @@ def reset_plan_opts():
 
 
 def set_route_buffer(t=None):
+    import torch
+    if t is not None:
+        _need(t, "route buffer", torch.int32)
     _check(lib().itk_set_route_buffer(_ptr(t), 0 if t is None else t.numel()), "itk_set_route_buffer")
 
 
 def set_count_buffer(t=None):
+    import torch
+    if t is not None:
+        _need(t, "count buffer", torch.int32)
     _check(lib().itk_set_count_buffer(_ptr(t), 0 if t is None else t.numel()), "itk_set_count_buffer")
 
 
