@@ -9,37 +9,44 @@
 // workgroup share every staged key tile):
 //  * contraction: v_mfma_f32_32x32x16_{bf16,f16} (v_mfma_f32_32x32x2f32 for
 //    fp32 inputs; v_mfma_scale_f32_32x32x64_f8f6f4 when FP8 keys are scored
-//    with per-row quantized FP8 queries).  MFMA rows are the query's heads (one or two 32-head
-//    blocks), columns are 32 keys; the query's Q fragments stay in VGPRs for
-//    the whole scan, K tiles of 64 keys are staged once per workgroup into a
-//    padded, double-buffered LDS tile (FP8 keys are widened to the MFMA
-//    operand type while staging; the per-key scale is applied after the head
-//    reduction, which is exact for non-negative scales).
+//    with per-row quantized FP8 queries).  MFMA rows are the query's heads
+//    (one or two 32-head blocks), columns are 32 keys; the query's Q
+//    fragments stay in VGPRs for the whole scan.  Key stages are copied once
+//    per workgroup into padded, double-buffered LDS rows: 16- and 32-bit keys
+//    (and FP8 keys scored as FP8) by direct global -> LDS loads, 128 keys per
+//    stage for rows of up to 256 bytes; FP8 keys scored in bf16/fp16 go
+//    through registers, 64 keys per stage, and are widened exactly on the
+//    way.  The per-key FP8 scale is applied after the head reduction, which
+//    is exact for non-negative scales.
 //  * epilogue in registers: each lane owns 16 head rows of one key column per
 //    32x32 block; w * max(acc, 0) is accumulated in-lane and the two half-waves
 //    are combined with one cross-lane exchange, leaving lane l with the score
-//    of key tile_start + l.
+//    of key tile_start + l.  The MFMAs of each 32-key block are interleaved
+//    with the epilogue of the block before it.
 //  * sample -> filter -> refresh -> select (LiteTopK Sec. 3.2): a tile-strided
-//    view of each row is scored first (two light passes: the score range,
-//    with the view's scores stored when they fit the candidate buffer's
-//    bytes, then an equal-width histogram of m = 2048 bins over
-//    [s_min, s_max] from the stored scores, or from a second scoring); the
-//    threshold bin starts at the bin of the sample's rank-q score, q sized
-//    for rho * k of the row (the rank calibration of the Sample-Guided paper,
-//    Sec. 4.2).  In the scan, bin = floor((s - s_min) * delta) is one FMA; a
-//    key passes if its bin is not below the threshold bin; passing keys are
-//    compacted with a wave ballot + popcount + lane rank into a per-wave LDS
-//    staging list that is flushed 64 entries at a time with one atomic on the
-//    row's candidate tail, and counted in the wave's LDS histogram; the
-//    threshold bin then moves up one bin at a time while the admitted keys
-//    strictly above it number at least k.
+//    view of each row (or, with a history sample, a caller-given key list) is
+//    scored first in two light passes: the score range, with the scores
+//    stored when they fit the candidate buffer's bytes, then an equal-width
+//    histogram of m = 2048 bins over [s_min, s_max].  The threshold bin
+//    starts at the bin of the sample's rank-q score, q sized for rho * k of
+//    the row (the rank calibration of the Sample-Guided paper, Sec. 4.2).  In
+//    the scan, bin = floor((s - s_min) * delta) is one FMA; a key passes if
+//    its bin is not below the threshold bin; passing keys are compacted with
+//    a wave ballot + popcount + lane rank into a per-wave LDS staging list
+//    that is flushed 64 entries at a time with one atomic on the row's
+//    candidate tail, and counted in the wave's LDS histogram; the threshold
+//    bin then moves up one bin at a time while the admitted keys strictly
+//    above it number at least k.  Under key splits a split that raises its
+//    bin publishes it to the row's word (atomic max) and the row's other
+//    splits move up to it.
+//  * recovery: rows whose candidates overflowed the buffer or fell short of
+//    min(k, L) are re-scored by the whole grid (a full-row histogram on the
+//    sampled bin map, then a pass that collects every key at or above its
+//    k-th bin), so sampling never decides the result.
 //  * select: one workgroup per row gathers the row's candidates into LDS,
 //    commits every value-histogram bin above the boundary bin and settles the
-//    boundary bin exactly (ranking or composite-key radix refinement); rows
-//    whose candidates overflowed
-//    the buffer or fell short of k are re-scored from Q and K and selected
-//    exactly from the full row (recovery), so sampling never decides the
-//    result.
+//    boundary bin exactly (ranking or composite-key radix refinement); a row
+//    whose boundary bin alone still overflows the buffer is re-scored there.
 #pragma once
 
 #include "itk_device.hpp"
