@@ -138,6 +138,9 @@ itk_status topk_ragged_noalloc(const float *scores, int64_t row_pitch, const int
  *            finite and >= 0 (the scale is applied after the ReLU, which is
  *            exact only for non-negative scales).
  *   W        [T, H] fp32 per-query head weights.
+ *            Q, K and W must be finite, and the scores must not overflow
+ *            fp32: a NaN or infinite score is a precondition violation, as
+ *            NaN is for topk_ragged (the result is then unspecified).
  *   kv_len   [T] int32 (device).
  *   out_idx  [T, k] int32: selected key indices in unspecified order, -1 pad.
  *   out_score[T, k] fp32: the kernel's fp32 score of out_idx, -inf pad.
