@@ -174,7 +174,8 @@ struct FusedArgs {
     Cand *cand;        // [T][cap] (head rows) or [T][P][capS] (single head)
     float *samp;       // [T][samp_cap] scores of the sampled view (both paths)
     uint32_t *hist_r;  // [T][NBINS] full-row histogram of rows under recovery (head rows)
-    uint32_t *rflag;   // [T] 1 when the row went through the grid-wide recovery (head rows)
+    uint32_t *rflag;   // [T] 1 when the row takes a recovery route (head rows: the grid-wide
+                       // recovery; single head: the re-scoring kernel)
     uint32_t *gpub;    // [T] gate bin published across the key splits of a row (head rows)
     // single-head (query-column) path
     float *gate;       // [T] admission gate (score space)
@@ -1582,6 +1583,16 @@ struct RescoreSrc {
 
 enum { FROUTE_SAMPLE = 1, FROUTE_RECOVER = 3, FROUTE_ALL = 4, FROUTE_GRID_RECOVERY = 5 };
 
+// After the grid-wide recovery passes every row holds at least min(k, L)
+// candidates; a row whose candidates still overflow the buffer (its boundary
+// bin alone holds more keys than the buffer) is re-scored from Q and K by
+// k_fused_rescore instead of being selected from the buffer.
+__device__ __forceinline__ bool select_rescores(const FusedArgs &a, int t, uint32_t need)
+{
+    const uint32_t n = a.tail[t];
+    return n > (uint32_t)a.cap || n < need;
+}
+
 template <class C>
 __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
 {
@@ -1601,11 +1612,8 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
         if (tid == 0 && a.count) a.count[t] = 0;
         return;
     }
-    // After the grid-wide recovery passes every row holds at least min(k, L)
-    // candidates; a row whose candidates still overflow the buffer is
-    // re-scored here.
     const uint32_t n = a.tail[t];
-    const bool recover = n > (uint32_t)a.cap || n < need;
+    const bool recover = select_rescores(a, t, need);  // left to k_fused_rescore
     auto emit = [&](uint32_t slot, uint64_t K) {
         if (slot < need) {
             oi[slot] = (int32_t)key_index(K);
@@ -1647,9 +1655,6 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
         } else {
             exact_select<SEL_THREADS_HR>(sm, src, need, emit);
         }
-    } else {
-        RescoreSrc<C> src{&a, t, L};
-        exact_select<SEL_THREADS_HR>(sm, src, need, emit);
     }
     if (tid == 0 && a.count) a.count[t] = (int32_t)n;
     if (tid == 0 && a.route) {
@@ -1657,6 +1662,37 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
         const RowSample rs = row_sample(a, t, t / FUSED_WAVES, L, bp.z != 0.f);
         a.route[t] = recover ? FROUTE_RECOVER
                              : (a.rflag[t] ? FROUTE_GRID_RECOVERY : (rs.admit_all ? FROUTE_ALL : FROUTE_SAMPLE));
+    }
+}
+
+// The re-scoring route of the selection, for the rows select_rescores
+// names: every valid key of the row is re-scored from Q and K (RescoreSrc,
+// the scan's MFMA order, so the scores equal the scan's) and the row is
+// selected exactly by one workgroup.  A kernel of its own, so that the
+// selection does not carry the re-scoring registers (Q fragments and
+// accumulators) on every row.  Such rows are rare, so RESCORE_GROUPS
+// workgroups walk the rows (workgroup b takes rows b, b + gridDim.x, ...)
+// instead of one workgroup per row, which keeps the launch cheap when there
+// is nothing to do.
+template <class C>
+__global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_rescore(FusedArgs a)
+{
+    __shared__ SelectSmem sm;
+    for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
+        const uint32_t L = kv_length(a, t);
+        const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+        if (need == 0 || !select_rescores(a, t, need)) continue;  // workgroup-uniform
+        int32_t *oi = a.out_idx + (size_t)t * a.k;
+        float *os = a.out_score + (size_t)t * a.k;
+        auto emit = [&](uint32_t slot, uint64_t K) {
+            if (slot < need) {
+                oi[slot] = (int32_t)key_index(K);
+                os[slot] = key_value(K);
+            }
+        };
+        RescoreSrc<C> src{&a, t, L};
+        exact_select<SEL_THREADS_HR>(sm, src, need, emit);
+        __syncthreads();  // the next row reuses sm
     }
 }
 
@@ -1700,6 +1736,12 @@ hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t 
     {
         StageTimer st(ST_F_SELECT, stream);
         e = launch_kernel(k_fused_select<C>, dim3(p.T), dim3(SEL_THREADS_HR), stream, a);
+    }
+    if (e != hipSuccess) return e;
+    {
+        StageTimer st(ST_F_RESCORE, stream);
+        e = launch_kernel(k_fused_rescore<C>, dim3(p.T < RESCORE_GROUPS ? p.T : RESCORE_GROUPS), dim3(SEL_THREADS_HR),
+                          stream, a);
     }
     return e;
 }

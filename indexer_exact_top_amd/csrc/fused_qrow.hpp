@@ -506,7 +506,7 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_qrow_main(FusedArgs a)
         if (qq.t[qb] < a.T) a.qcnt[((size_t)qq.t[qb] * a.P + p) * 2 + h] = cnt[qb];
 }
 
-// ------------------------------------------- select (+ recovery) per query
+// --------------------------------------- select, and re-scoring per query
 // Every valid key of query t, re-scored with the same operand layout as the
 // scan (the query in column 0 of the B operand, 32 keys per MFMA as rows), so
 // that every score equals the scan's.  Lanes 0 and 32 hold the results.
@@ -610,6 +610,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
     if (need == 0) {
         if (tid == 0 && a.route) a.route[t] = 4;
         if (tid == 0 && a.count) a.count[t] = 0;
+        if (tid == 0) a.rflag[t] = 0u;
         return;
     }
     // slice counts -> prefix (cpre) and overflow flag: one slice per thread,
@@ -630,7 +631,10 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
     }
     __syncthreads();
     const uint32_t n = cpre[ncell];
+    // a query whose slices overflowed or hold fewer than min(k, L)
+    // candidates is left to k_qrow_rescore
     const bool recover = a.force == 1 || s_ovf || n < need;
+    if (tid == 0) a.rflag[t] = recover ? 1u : 0u;
     if (tid == 0 && a.count) {  // admitted candidates, past the slices' capacity included
         uint32_t tot = 0;
         for (int c = 0; c < ncell; ++c) tot += cnt[c];
@@ -687,11 +691,37 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
     } else if (!recover) {
         QRowSliceSrc src{a.cand + (size_t)t * ncell * capH, cpre, ncell, capH};
         exact_select<NT>(sm, src, need, emit);
-    } else {
-        QRowRescoreSrc<C> src{&a, t, L};
-        exact_select<NT>(sm, src, need, emit);
     }
     if (tid == 0 && a.route) a.route[t] = recover ? 3 : 1;
+}
+
+// The re-scoring route of the single-head selection, for the queries that
+// k_qrow_select flagged: every valid key of the query is re-scored from Q
+// and K (QRowRescoreSrc, the scan's operand layout, so the scores equal the
+// scan's) and the query is selected exactly by one workgroup.  A kernel of
+// its own, so that the selection does not carry the re-scoring registers on
+// every query (they made it spill).  RESCORE_GROUPS workgroups walk the
+// queries, so that the launch stays cheap when no query is flagged.
+template <class C>
+__global__ __launch_bounds__(SEL_THREADS) void k_qrow_rescore(FusedArgs a)
+{
+    __shared__ SelectSmemT<QROW_STASH> sm;
+    for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
+        if (!a.rflag[t]) continue;  // workgroup-uniform
+        const uint32_t L = kv_length(a, t);
+        const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+        int32_t *oi = a.out_idx + (size_t)t * a.k;
+        float *os = a.out_score + (size_t)t * a.k;
+        auto emit = [&](uint32_t slot, uint64_t K) {
+            if (slot < need) {
+                oi[slot] = (int32_t)key_index(K);
+                os[slot] = key_value(K);
+            }
+        };
+        QRowRescoreSrc<C> src{&a, t, L};
+        exact_select<SEL_THREADS>(sm, src, need, emit);
+        __syncthreads();  // the next query reuses sm
+    }
 }
 
 // --------------------------------------------------------------- launch
@@ -717,6 +747,12 @@ hipError_t launch_qrow_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t s
     {
         StageTimer st(ST_F_SELECT, stream);
         e = launch_kernel(k_qrow_select<C>, dim3(p.T), dim3(SEL_THREADS), stream, a);
+    }
+    if (e != hipSuccess) return e;
+    {
+        StageTimer st(ST_F_RESCORE, stream);
+        e = launch_kernel(k_qrow_rescore<C>, dim3(p.T < RESCORE_GROUPS ? p.T : RESCORE_GROUPS), dim3(SEL_THREADS),
+                          stream, a);
     }
     return e;
 }

@@ -54,7 +54,7 @@ bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
 const char *const g_stage_names[ST_COUNT] = {"ragged_scan",      "ragged_finish", "fused_sample_range",
                                              "fused_sample_hist", "fused_main",    "fused_select",
-                                             "ragged_rowlocal", "fused_recover"};
+                                             "ragged_rowlocal", "fused_recover",    "fused_rescore"};
 }  // namespace
 
 StageTimer::StageTimer(int stage_id, hipStream_t s) : stage(-1), stream(s)
@@ -154,6 +154,7 @@ itk_status plan_fused(int32_t T, int32_t H, int32_t D, int64_t N, int32_t k, itk
         p.off_gate = off; off = align256(off + (size_t)T * sizeof(float));
         p.off_qcnt = off; off = align256(off + (size_t)T * P * 2 * sizeof(uint32_t));
         p.off_cand = off; off = align256(off + (size_t)T * P * capS * sizeof(Cand));
+        p.off_rflag = off; off = align256(off + (size_t)T * sizeof(uint32_t));
         p.bytes = off;
         *out = p;
         return ITK_OK;
@@ -263,7 +264,7 @@ hipError_t launch_fused(const FusedPlan &p, const void *Q, const void *K, const 
     a.sample_tiles = p.sample_tiles; a.force = p.force; a.rho = p.rho;
     a.samp = p.samp_cap > 0 ? reinterpret_cast<float *>(w + p.off_samp) : nullptr;
     a.hist_r = p.qrow ? nullptr : reinterpret_cast<uint32_t *>(w + p.off_hist_r);
-    a.rflag = p.qrow ? nullptr : reinterpret_cast<uint32_t *>(w + p.off_rflag);
+    a.rflag = reinterpret_cast<uint32_t *>(w + p.off_rflag);
     a.gpub = p.qrow ? nullptr : reinterpret_cast<uint32_t *>(w + p.off_gpub);
     a.samp_cap = p.samp_cap;
     a.gate = nullptr; a.qcnt = nullptr; a.capS = 0;

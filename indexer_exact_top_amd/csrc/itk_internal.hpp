@@ -125,6 +125,7 @@ constexpr int TILE_KEYS = 64;
 // 128 VGPRs per lane, which makes it spill).
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_THREADS_HR = 512;
+constexpr int RESCORE_GROUPS = 256;  // workgroups of the re-scoring kernels (rows are walked)
 constexpr int QROW_MAX_SPLITS = 256;  // single-head path: key splits per query
 // Head-rows path with at most KP_MAX_T queries: the main pass runs one key
 // range per wave, about KP_WAVES waves in all (two per SIMD).  Measured on
@@ -189,6 +190,7 @@ struct StageTimer {
     StageTimer(int stage_id, hipStream_t s);
     ~StageTimer();
 };
-enum Stage { ST_RAG_SCAN = 0, ST_RAG_FINISH, ST_F_MINMAX, ST_F_HIST, ST_F_MAIN, ST_F_SELECT, ST_RAG_ROWLOCAL, ST_F_RECOVER, ST_COUNT };
+enum Stage { ST_RAG_SCAN = 0, ST_RAG_FINISH, ST_F_MINMAX, ST_F_HIST, ST_F_MAIN, ST_F_SELECT, ST_RAG_ROWLOCAL, ST_F_RECOVER, ST_F_RESCORE,
+             ST_COUNT };
 
 }  // namespace itk
