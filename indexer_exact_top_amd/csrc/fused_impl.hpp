@@ -997,10 +997,13 @@ __device__ __forceinline__ uint32_t bin_of(float b)
 // Bins the view scores that pass A stored (the same tiles of the same split,
 // so every score is counted once), or, when the plan stores no view (a view
 // larger than the candidate buffer), scores the view again.
-template <class C>
+// STORED: pass A stored the sampled scores (the planner decides), so this
+// pass only reads them; the other instantiation scores the sample again.
+// Separate instantiations, so that the reading one carries neither the
+// scoring registers nor the key stages.
+template <class C, bool STORED>
 __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
 {
-    __shared__ TileBuf<C> tb;
     __shared__ uint32_t whist[FUSED_WAVES][NBINS];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int g, p;
@@ -1019,7 +1022,8 @@ __global__ __launch_bounds__(FUSED_THREADS) void k_fused_samplehist(FusedArgs a)
     const SampleIter it = sample_iter(a, g, p, maxL);
     // a degenerate sampled range leaves the gate open: nothing to count
     const bool count = active && bp.z == 0.f;
-    if (!a.samp) {  // workgroup-uniform
+    if constexpr (!STORED) {
+        __shared__ TileBuf<C, 1> tb;
         QFrags<C> qf;
         if (active) qf.load(a, t);
         scan_tiles<C, 1>(a, tb, qf, it.first_key, it.stride_keys, it.ntiles, it.end, count, L,
@@ -1715,7 +1719,8 @@ hipError_t launch_fused_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t 
     if (e != hipSuccess) return e;
     {
         StageTimer st(ST_F_HIST, stream);
-        e = launch_kernel(k_fused_samplehist<C>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a);
+        e = a.samp ? launch_kernel(k_fused_samplehist<C, true>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a)
+                   : launch_kernel(k_fused_samplehist<C, false>, dim3(p.G * p.Ps), dim3(FUSED_THREADS), stream, a);
     }
     if (e != hipSuccess) return e;
     {
