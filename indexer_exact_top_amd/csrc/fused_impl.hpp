@@ -1669,34 +1669,55 @@ __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_select(FusedArgs a)
     }
 }
 
+// Re-scores row t from Q and K and selects it exactly (one workgroup).
+template <class C>
+__device__ void rescore_row(const FusedArgs &a, int t, SelectSmem &sm)
+{
+    const uint32_t L = kv_length(a, t);
+    const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+    int32_t *oi = a.out_idx + (size_t)t * a.k;
+    float *os = a.out_score + (size_t)t * a.k;
+    auto emit = [&](uint32_t slot, uint64_t K) {
+        if (slot < need) {
+            oi[slot] = (int32_t)key_index(K);
+            os[slot] = key_value(K);
+        }
+    };
+    RescoreSrc<C> src{&a, t, L};
+    exact_select<SEL_THREADS_HR>(sm, src, need, emit);
+    __syncthreads();  // the next row reuses sm
+}
+
+__device__ __forceinline__ bool row_rescores(const FusedArgs &a, int t)
+{
+    const uint32_t L = kv_length(a, t);
+    const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+    return need != 0 && select_rescores(a, t, need);
+}
+
 // The re-scoring route of the selection, for the rows select_rescores
 // names: every valid key of the row is re-scored from Q and K (RescoreSrc,
 // the scan's MFMA order, so the scores equal the scan's) and the row is
 // selected exactly by one workgroup.  A kernel of its own, so that the
 // selection does not carry the re-scoring registers (Q fragments and
-// accumulators) on every row.  Such rows are rare, so RESCORE_GROUPS
-// workgroups walk the rows (workgroup b takes rows b, b + gridDim.x, ...)
-// instead of one workgroup per row, which keeps the launch cheap when there
-// is nothing to do.
+// accumulators) on every row.  Such rows are rare: RESCORE_GROUPS workgroups
+// share the rows (workgroup b takes rows b, b + gridDim.x, ...), and each
+// checks its rows a chunk of one row per thread at a time, with one vote, so
+// that a call with nothing to re-score costs about one memory round trip.
 template <class C>
 __global__ __launch_bounds__(SEL_THREADS_HR) void k_fused_rescore(FusedArgs a)
 {
     __shared__ SelectSmem sm;
-    for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
-        const uint32_t L = kv_length(a, t);
-        const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
-        if (need == 0 || !select_rescores(a, t, need)) continue;  // workgroup-uniform
-        int32_t *oi = a.out_idx + (size_t)t * a.k;
-        float *os = a.out_score + (size_t)t * a.k;
-        auto emit = [&](uint32_t slot, uint64_t K) {
-            if (slot < need) {
-                oi[slot] = (int32_t)key_index(K);
-                os[slot] = key_value(K);
-            }
-        };
-        RescoreSrc<C> src{&a, t, L};
-        exact_select<SEL_THREADS_HR>(sm, src, need, emit);
-        __syncthreads();  // the next row reuses sm
+    for (int base = 0; blockIdx.x + (int64_t)base * gridDim.x < a.T; base += SEL_THREADS_HR) {
+        const int64_t ti = blockIdx.x + (int64_t)(base + threadIdx.x) * gridDim.x;
+        if (!__syncthreads_or(ti < a.T && row_rescores(a, (int)ti))) continue;
+        for (int j = 0; j < SEL_THREADS_HR; ++j) {
+            const int64_t tj = blockIdx.x + (int64_t)(base + j) * gridDim.x;
+            if (tj >= a.T) break;
+            const int t = (int)tj;
+            if (!row_rescores(a, t)) continue;  // workgroup-uniform
+            rescore_row<C>(a, t, sm);
+        }
     }
 }
 

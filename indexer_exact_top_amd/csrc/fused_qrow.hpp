@@ -700,27 +700,36 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
 // and K (QRowRescoreSrc, the scan's operand layout, so the scores equal the
 // scan's) and the query is selected exactly by one workgroup.  A kernel of
 // its own, so that the selection does not carry the re-scoring registers on
-// every query (they made it spill).  RESCORE_GROUPS workgroups walk the
-// queries, so that the launch stays cheap when no query is flagged.
+// every query (they made it spill).  RESCORE_GROUPS workgroups share the
+// queries (workgroup b takes queries b, b + gridDim.x, ...) and check them a
+// chunk of one query per thread at a time, with one vote, so that a call
+// with no flagged query costs about one memory round trip.
 template <class C>
 __global__ __launch_bounds__(SEL_THREADS) void k_qrow_rescore(FusedArgs a)
 {
     __shared__ SelectSmemT<QROW_STASH> sm;
-    for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
-        if (!a.rflag[t]) continue;  // workgroup-uniform
-        const uint32_t L = kv_length(a, t);
-        const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
-        int32_t *oi = a.out_idx + (size_t)t * a.k;
-        float *os = a.out_score + (size_t)t * a.k;
-        auto emit = [&](uint32_t slot, uint64_t K) {
-            if (slot < need) {
-                oi[slot] = (int32_t)key_index(K);
-                os[slot] = key_value(K);
-            }
-        };
-        QRowRescoreSrc<C> src{&a, t, L};
-        exact_select<SEL_THREADS>(sm, src, need, emit);
-        __syncthreads();  // the next query reuses sm
+    for (int base = 0; blockIdx.x + (int64_t)base * gridDim.x < a.T; base += SEL_THREADS) {
+        const int64_t ti = blockIdx.x + (int64_t)(base + threadIdx.x) * gridDim.x;
+        if (!__syncthreads_or(ti < a.T && a.rflag[ti] != 0u)) continue;
+        for (int j = 0; j < SEL_THREADS; ++j) {
+            const int64_t tj = blockIdx.x + (int64_t)(base + j) * gridDim.x;
+            if (tj >= a.T) break;
+            const int t = (int)tj;
+            if (!a.rflag[t]) continue;  // workgroup-uniform
+            const uint32_t L = kv_length(a, t);
+            const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
+            int32_t *oi = a.out_idx + (size_t)t * a.k;
+            float *os = a.out_score + (size_t)t * a.k;
+            auto emit = [&](uint32_t slot, uint64_t K) {
+                if (slot < need) {
+                    oi[slot] = (int32_t)key_index(K);
+                    os[slot] = key_value(K);
+                }
+            };
+            QRowRescoreSrc<C> src{&a, t, L};
+            exact_select<SEL_THREADS>(sm, src, need, emit);
+            __syncthreads();  // the next query reuses sm
+        }
     }
 }
 
