@@ -585,6 +585,7 @@ struct QRowSliceSrc {
 };
 
 constexpr int QROW_STASH = 16384;  // candidates kept on chip by the single-head select
+constexpr int QROW_RESCORE_THREADS = 512;
 
 template <class C>
 __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
@@ -700,18 +701,19 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_select(FusedArgs a)
 // and K (QRowRescoreSrc, the scan's operand layout, so the scores equal the
 // scan's) and the query is selected exactly by one workgroup.  A kernel of
 // its own, so that the selection does not carry the re-scoring registers on
-// every query (they made it spill).  RESCORE_GROUPS workgroups share the
+// every query (they made it spill), with 512 threads, whose register budget
+// holds the re-scoring without spills.  RESCORE_GROUPS workgroups share the
 // queries (workgroup b takes queries b, b + gridDim.x, ...) and check them a
 // chunk of one query per thread at a time, with one vote, so that a call
 // with no flagged query costs about one memory round trip.
 template <class C>
-__global__ __launch_bounds__(SEL_THREADS) void k_qrow_rescore(FusedArgs a)
+__global__ __launch_bounds__(QROW_RESCORE_THREADS) void k_qrow_rescore(FusedArgs a)
 {
     __shared__ SelectSmemT<QROW_STASH> sm;
-    for (int base = 0; blockIdx.x + (int64_t)base * gridDim.x < a.T; base += SEL_THREADS) {
+    for (int base = 0; blockIdx.x + (int64_t)base * gridDim.x < a.T; base += QROW_RESCORE_THREADS) {
         const int64_t ti = blockIdx.x + (int64_t)(base + threadIdx.x) * gridDim.x;
         if (!__syncthreads_or(ti < a.T && a.rflag[ti] != 0u)) continue;
-        for (int j = 0; j < SEL_THREADS; ++j) {
+        for (int j = 0; j < QROW_RESCORE_THREADS; ++j) {
             const int64_t tj = blockIdx.x + (int64_t)(base + j) * gridDim.x;
             if (tj >= a.T) break;
             const int t = (int)tj;
@@ -727,7 +729,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_qrow_rescore(FusedArgs a)
                 }
             };
             QRowRescoreSrc<C> src{&a, t, L};
-            exact_select<SEL_THREADS>(sm, src, need, emit);
+            exact_select<QROW_RESCORE_THREADS>(sm, src, need, emit);
             __syncthreads();  // the next query reuses sm
         }
     }
@@ -760,7 +762,7 @@ hipError_t launch_qrow_cfg(const FusedPlan &p, const FusedArgs &a, hipStream_t s
     if (e != hipSuccess) return e;
     {
         StageTimer st(ST_F_RESCORE, stream);
-        e = launch_kernel(k_qrow_rescore<C>, dim3(p.T < RESCORE_GROUPS ? p.T : RESCORE_GROUPS), dim3(SEL_THREADS),
+        e = launch_kernel(k_qrow_rescore<C>, dim3(p.T < RESCORE_GROUPS ? p.T : RESCORE_GROUPS), dim3(QROW_RESCORE_THREADS),
                           stream, a);
     }
     return e;
