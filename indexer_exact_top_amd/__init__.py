@@ -355,10 +355,11 @@ def profile_read():
 
 
 # ------------------------------------------------------------ test probes
-def debug_mfma(mtype: int, a_frags, b_frags):
-    """One 32x32 MFMA on per-lane fragments; returns float32 [64, 16]."""
+def debug_mfma(mtype: int, a_frags, b_frags, acc=None):
+    """One 32x32 MFMA on per-lane fragments; returns float32 [64, 16]
+    (mtype 4: the FP8 MFMA onto the accumulator values ``acc`` [64, 16])."""
     import torch
-    c = torch.empty((64, 16), dtype=torch.float32, device=a_frags.device)
+    c = torch.empty((64, 16), dtype=torch.float32, device=a_frags.device) if acc is None else acc.clone()
     _check(lib().itk_debug_mfma(mtype, _ptr(a_frags), _ptr(b_frags), _ptr(c), _stream(None)), "itk_debug_mfma")
     return c
 

@@ -15,6 +15,20 @@ __global__ void k_debug_mfma(const typename MTraits<MT>::frag *a, const typename
     for (int r = 0; r < 16; ++r) c[l * 16 + r] = acc[r];
 }
 
+// The FP8 MFMA with an accumulator input: lane l's 16 accumulator values
+// start from c[l*16 .. l*16+15] (the chained k-steps of the FP8 scan add
+// onto the previous step's sums).
+__global__ void k_debug_mfma_fp8_acc(const u32x8_t *a, const u32x8_t *b, float *c)
+{
+    const int l = threadIdx.x;
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = c[l * 16 + r];
+    acc = mfma32<M_FP8>(a[l], b[l], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[l * 16 + r] = acc[r];
+}
+
 // Widens codes 4 at a time, as the key staging does (a partial last group
 // is padded with zero codes, which are not stored).
 __global__ void k_debug_fp8(const uint8_t *in, uint16_t *bf, uint16_t *hf, int n)
@@ -88,6 +102,12 @@ itk_status itk_debug_mfma(int32_t mtype, const void *a_frags, const void *b_frag
     else if (mtype == M_F32)
         e = launch_kernel(k_debug_mfma<M_F32>, dim3(1), dim3(64), s, static_cast<const float *>(a_frags),
                           static_cast<const float *>(b_frags), c_out);
+    else if (mtype == M_FP8)
+        e = launch_kernel(k_debug_mfma<M_FP8>, dim3(1), dim3(64), s, static_cast<const u32x8_t *>(a_frags),
+                          static_cast<const u32x8_t *>(b_frags), c_out);
+    else if (mtype == M_FP8 + 1)
+        e = launch_kernel(k_debug_mfma_fp8_acc, dim3(1), dim3(64), s, static_cast<const u32x8_t *>(a_frags),
+                          static_cast<const u32x8_t *>(b_frags), c_out);
     else
         return ITK_ERR_INVALID_ARG;
     return e == hipSuccess ? ITK_OK : ITK_ERR_HIP;
