@@ -89,7 +89,10 @@ typedef enum {
  * complete-row pass certifies it and collects the admitted candidates, and an
  * exact radix refinement over (ordered fp32 key, inverted index) resolves the
  * final set; underfilled views fall back to a band pass and then to an exact
- * route that needs no sample (Sec. 4.2-4.4 of the same paper).
+ * route that needs no sample (Sec. 4.2-4.4 of the same paper).  A short row
+ * (at most 7680 valid entries, the on-chip stash) may instead be refined
+ * whole without a view, where the planner finds that faster (the row-local
+ * exact mapping of Sec. 5.5).
  * ------------------------------------------------------------------------ */
 size_t topk_ragged_workspace_size(int32_t M, int64_t row_pitch, int32_t k);
 
@@ -251,9 +254,13 @@ typedef struct {
                                2 ragged: force the band pass */
     int32_t ragged_route;   /* ragged mapping: 0 auto (by shape), 1 segments
                                (view + scan per segment, finish per row),
-                               2 row-local (one workgroup per row); row-local
-                               is taken only for rows of at most 262144 scores
-                               and rho1 * k <= 4096 */
+                               2 row-local (one workgroup per row, sampled
+                               steps for every row), 3 row-local with the
+                               direct-exact steps (no view) for every row of
+                               at most 7680 valid scores (or `capacity`);
+                               row-local is taken only for rows of at most
+                               262144 scores and rho1 * k <= 4096, or a
+                               pitch of at most 7680 */
 } itk_plan_opts;
 
 /* NULL restores the defaults. */

@@ -488,7 +488,7 @@ itk_status itk_set_plan_opts(const itk_plan_opts *o)
         return ITK_OK;
     }
     if (o->sample_stride < 0 || o->capacity < 0 || o->splits < 0 || o->force_route < 0 || o->force_route > 2 ||
-        o->ragged_route < 0 || o->ragged_route > 2 ||
+        o->ragged_route < 0 || o->ragged_route > 3 ||
         !(o->rho >= 0.f) || !(o->rho1 >= 0.f))
         return ITK_ERR_INVALID_ARG;
     if (o->sample_stride > 0 && o->sample_stride > 4096) return ITK_ERR_INVALID_ARG;

@@ -40,7 +40,7 @@ struct Knobs {
     int32_t capacity = 0;
     int32_t splits = 0;
     int32_t force_route = 0;
-    int32_t route_select = 0;  // ragged mapping: 0 auto, 1 segments, 2 row-local
+    int32_t route_select = 0;  // ragged mapping: 0 auto, 1 segments, 2 row-local, 3 row-local direct-exact
 };
 Knobs &knobs();
 
@@ -88,6 +88,12 @@ constexpr int RL_THREADS = RL_THREADS_DEF;
 constexpr int64_t RAG_RL_MAX_PITCH = 262144;
 constexpr int RAG_RL_MIN_ROWS = 512;
 constexpr int RAG_RL_MAX_CAND = 4096;
+// Row-local direct-exact steps (no view) for rows of at most rho1 * k +
+// RAG_DIRECT_MARGIN valid scores: refining an on-chip entry costs about
+// 1.3 ns of the workgroup's time and the view about 3.9 us (measured on
+// rows of 1K-7.7K scores), so the view pays only when it removes more than
+// about 3000 entries.
+constexpr int RAG_DIRECT_MARGIN = 3072;
 
 struct RaggedPlan {
     int32_t M = 0;
@@ -102,6 +108,7 @@ struct RaggedPlan {
     int32_t force = 0;
     bool rowlocal = false;   // one workgroup per row, candidates on chip
     int32_t rlcap = 0;       // row-local: on-chip candidate capacity
+    uint32_t direct_max = 0; // row-local: rows of at most this length are selected whole (no view)
     // workspace carve
     size_t off_cnt = 0, off_ep = 0, off_slices = 0, off_band = 0, off_order = 0, bytes = 0;
 };

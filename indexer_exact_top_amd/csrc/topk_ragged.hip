@@ -19,7 +19,11 @@
 //                   band pass over the row, an overflowing one the exact route
 //                   (Sec. 4.3, Table 2).  No global scratch, no second
 //                   launch; the hardware dispatcher hands rows to CUs as they
-//                   free up, which balances ragged lengths.
+//                   free up, which balances ragged lengths.  A row whose
+//                   valid entries all fit the stash skips the view and goes
+//                   whole into the stash (the direct-exact row-local mapping
+//                   of Sec. 5.5): rows of a pitch that fits take this
+//                   kernel at any row count.
 //
 // Longer rows (decoding against long contexts) are cut into segments:
 //
@@ -64,7 +68,9 @@ struct RaggedArgs {
     int64_t pitch, seg;
     int32_t M, k, P, subcap, bandcap, view_blocks, force;
     int32_t rlcap;   // row-local route: candidates kept on chip (<= STASH_CAP)
-    int32_t *order;  // row-local route: [M] rows by descending length (workgroup b takes row order[b])
+    uint32_t direct_max;  // row-local route: rows of at most this many scores are selected whole (no view)
+    int32_t *order;  // row-local route: [M] rows by descending length (workgroup b takes row order[b]),
+                     // or null: workgroup b takes row b
     float rho, rho1;
 };
 
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(RL_THREADS, 4) void k_ragged_rowlocal(RaggedArgs a)
     constexpr int U = RL_U;
     constexpr uint32_t CHUNK = (uint32_t)NT * U * 4;  // scores per chunk
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = a.order[blockIdx.x];
+    const int r = a.order ? a.order[blockIdx.x] : (int)blockIdx.x;
     const uint32_t L = row_length(a, r);
     const uint32_t need = L < (uint32_t)a.k ? L : (uint32_t)a.k;
     int32_t *out = a.out_idx + (size_t)r * a.k;
@@ -542,12 +548,21 @@ __global__ __launch_bounds__(RL_THREADS, 4) void k_ragged_rowlocal(RaggedArgs a)
     };
     f32x4_t xa[U], xb[U];
     const bool exact_only = a.force == 1;
+    // Direct-exact (SGTK Sec. 5.5, the row-local exact mapping): a row whose
+    // valid entries all fit the stash needs no view; every entry is admitted
+    // and the refinement runs on the whole row.  One read of the row.
+    const bool direct = L <= a.direct_max;
     if (!exact_only && n4) load_chunk(0, xa);
 
     // ---- view -> coarse histogram -> endpoints (as in the segmented scan)
     float e0 = __builtin_nanf(""), e1 = __builtin_nanf("");
     bool admit_all = false;
-    if (!exact_only) {
+    if (!exact_only && direct) {
+        e0 = -__builtin_inff();
+        admit_all = true;
+        if (tid == 0) s_cnt = 0u;
+        __syncthreads();
+    } else if (!exact_only) {
         for (int i = tid; i < NBINS; i += NT) sm.hist[i] = 0u;
         if (tid == 0) s_cnt = 0u;
         __syncthreads();
@@ -667,7 +682,7 @@ __global__ __launch_bounds__(RL_THREADS, 4) void k_ragged_rowlocal(RaggedArgs a)
         stream(e0, __builtin_nanf(""), true);
         __syncthreads();
         const uint32_t C0 = s_cnt;
-        if (C0 <= cap && C0 >= need && a.force != 2) {
+        if (C0 <= cap && C0 >= need && (a.force != 2 || direct)) {
             route = admit_all ? ROUTE_ALL : ROUTE_SAMPLE;
             n = C0;
         } else if (C0 <= cap) {
@@ -730,10 +745,24 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     // one workgroup, and a secondary count that leaves room in the on-chip
     // stash.  Tests pick a mapping with the ragged_route knob (a segment
     // count also selects the segmented route).
-    const bool rl_fits = pitch <= RAG_RL_MAX_PITCH && (double)p.rho1 * k <= (double)RAG_RL_MAX_CAND;
-    if (rl_fits && (kn.route_select == 2 || (kn.route_select == 0 && kn.splits == 0 && M >= RAG_RL_MIN_ROWS))) {
+    const int rlcap = kn.capacity > 0 && kn.capacity < STASH_CAP ? kn.capacity : STASH_CAP;
+    // A pitch that fits the stash takes the row-local mapping at any row
+    // count: one launch instead of two (rows of 1K-7.7K scores, 1 to 256
+    // rows: 7-12 us against 13-17 us segmented).
+    const bool fits_chip = pitch <= rlcap;
+    const bool rl_fits = pitch <= RAG_RL_MAX_PITCH && ((double)p.rho1 * k <= (double)RAG_RL_MAX_CAND || fits_chip);
+    if (rl_fits && (kn.route_select == 2 || kn.route_select == 3 ||
+                    (kn.route_select == 0 && kn.splits == 0 && (M >= RAG_RL_MIN_ROWS || fits_chip)))) {
         p.rowlocal = true;
-        p.rlcap = kn.capacity > 0 && kn.capacity < STASH_CAP ? kn.capacity : STASH_CAP;
+        p.rlcap = rlcap;
+        // Direct-exact rows: a row no longer than the sampled steps' expected
+        // candidate count plus RAG_DIRECT_MARGIN is refined whole (the view's
+        // latency exceeds refining the extra entries); route 3 takes every
+        // row that fits, route 2 none.
+        const double dmax = ceil((double)p.rho1 * k) + RAG_DIRECT_MARGIN;
+        p.direct_max = kn.route_select == 2 ? 0u
+                     : kn.route_select == 3 ? (uint32_t)rlcap
+                     : (uint32_t)(dmax < (double)rlcap ? dmax : (double)rlcap);
         p.P = 1;
         p.seg = pitch;
         p.off_order = 0;
@@ -798,15 +827,20 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
     a.M = p.M; a.k = p.k; a.P = p.P; a.subcap = p.subcap; a.bandcap = p.bandcap;
     a.view_blocks = p.view_blocks; a.force = p.force;
     a.rlcap = p.rlcap;
+    a.direct_max = p.direct_max;
     a.order = nullptr;
     a.rho = p.rho; a.rho1 = p.rho1;
     const bool vec = (p.pitch % 4 == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0);
     hipError_t e;
     if (p.rowlocal) {
         StageTimer st(ST_RAG_ROWLOCAL, stream);
-        a.order = reinterpret_cast<int32_t *>(w + p.off_order);
-        e = launch_kernel(k_ragged_order, dim3(1), dim3(RL_ORDER_THREADS), stream, a);
-        if (e != hipSuccess) return e;
+        // Below RAG_RL_MIN_ROWS rows every workgroup is resident at once, so
+        // the order would change nothing: workgroup b takes row b.
+        if (p.M >= RAG_RL_MIN_ROWS) {
+            a.order = reinterpret_cast<int32_t *>(w + p.off_order);
+            e = launch_kernel(k_ragged_order, dim3(1), dim3(RL_ORDER_THREADS), stream, a);
+            if (e != hipSuccess) return e;
+        }
         return vec ? launch_kernel(k_ragged_rowlocal<true>, dim3(p.M), dim3(RL_THREADS), stream, a)
                    : launch_kernel(k_ragged_rowlocal<false>, dim3(p.M), dim3(RL_THREADS), stream, a);
     }

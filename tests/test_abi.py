@@ -145,7 +145,9 @@ def test_plan_opts_validation():
     # the row-local route (many rows of at most 2^18 scores) keeps its candidates on chip: its
     # scratch is the row order, 4 B per row
     assert lib.topk_ragged_workspace_size(1024, 131072, 2048) <= 4096
-    assert lib.itk_set_plan_opts(ctypes.byref(itk.PlanOpts(0, 0, 0, 0, 0, 0, 3))) == 1
+    assert lib.itk_set_plan_opts(ctypes.byref(itk.PlanOpts(0, 0, 0, 0, 0, 0, 3))) == 0  # row-local direct-exact
+    assert lib.itk_set_plan_opts(ctypes.byref(itk.PlanOpts(0, 0, 0, 0, 0, 0, 4))) == 1
+    assert lib.itk_set_plan_opts(None) == 0
 
 
 def test_history_sample_validation():

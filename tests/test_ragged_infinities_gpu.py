@@ -48,7 +48,7 @@ def _rows(M, pitch, k, seed):
     return synth.RaggedCase(name="ragged_infinities", M=M, pitch=pitch, k=k, scores=x, row_len=lens)
 
 
-@pytest.mark.parametrize("route", [1, 2])          # segmented, row-local
+@pytest.mark.parametrize("route", [1, 2, 3])       # segmented, row-local, row-local direct-exact
 @pytest.mark.parametrize("M,pitch,k", [(8, 40_000, 512), (16, 9_000, 2048)])
 def test_infinities_select_exactly(itk, route, M, pitch, k):
     itk.set_plan_opts(ragged_route=route)

@@ -52,7 +52,7 @@ def _fused_case(i):
     return case, fp8_score
 
 
-@pytest.mark.parametrize("route", [0, 2], ids=["auto", "rowlocal"])
+@pytest.mark.parametrize("route", [0, 2, 3], ids=["auto", "rowlocal", "direct"])
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_ragged(itk, i, route):
     case = _ragged_case(i)

@@ -1,8 +1,10 @@
 """topk_ragged on the GPU: bit-exact index sets against the CPU oracle.
 
-Every test runs under both mappings of the selector: segments (view and scan
-per segment, finish per row) and row-local (one workgroup per row); rows
-longer than the row-local limit take the segments either way."""
+Every test runs under each mapping of the selector: segments (view and scan
+per segment, finish per row), row-local (one workgroup per row, sampled
+steps) and row-local with the direct-exact steps for every row that fits the
+on-chip stash (no view); rows longer than the row-local limit take the
+segments either way."""
 import numpy as np
 import pytest
 import torch
@@ -29,7 +31,7 @@ def _run(itk, case, routes=False):
     return out.cpu().numpy(), (rb.cpu().numpy() if routes else None)
 
 
-@pytest.fixture(autouse=True, params=[1, 2], ids=["segments", "rowlocal"])
+@pytest.fixture(autouse=True, params=[1, 2, 3], ids=["segments", "rowlocal", "direct"])
 def route(request, itk):
     itk.reset_plan_opts()
     itk.set_plan_opts(ragged_route=request.param)
