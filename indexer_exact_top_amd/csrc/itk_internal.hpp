@@ -94,6 +94,11 @@ constexpr int RAG_RL_MAX_CAND = 4096;
 // rows of 1K-7.7K scores), so the view pays only when it removes more than
 // about 3000 entries.
 constexpr int RAG_DIRECT_MARGIN = 3072;
+// Row-local stashes for short pitches (a pitch of at most RL_TINY_CAP scores
+// takes that stash, else one of at most RL_SMALL_CAP the small one, else
+// STASH_CAP).
+constexpr int RL_TINY_CAP = 2048;
+constexpr int RL_SMALL_CAP = 4096;
 
 struct RaggedPlan {
     int32_t M = 0;
@@ -107,6 +112,7 @@ struct RaggedPlan {
     float rho = 1.5f, rho1 = 1.75f;
     int32_t force = 0;
     bool rowlocal = false;   // one workgroup per row, candidates on chip
+    int32_t rlstash = 0;     // row-local: stash entries of the kernel instance
     int32_t rlcap = 0;       // row-local: on-chip candidate capacity
     uint32_t direct_max = 0; // row-local: rows of at most this length are selected whole (no view)
     // workspace carve

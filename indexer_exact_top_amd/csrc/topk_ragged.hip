@@ -23,7 +23,8 @@
 //                   valid entries all fit the stash skips the view and goes
 //                   whole into the stash (the direct-exact row-local mapping
 //                   of Sec. 5.5): rows of a pitch that fits take this
-//                   kernel at any row count.
+//                   kernel at any row count, with a smaller stash for
+//                   short pitches (more workgroups per CU).
 //
 // Longer rows (decoding against long contexts) are cut into segments:
 //
@@ -500,10 +501,13 @@ __global__ __launch_bounds__(RL_ORDER_THREADS) void k_ragged_order(RaggedArgs a)
     for (int r = tid; r < a.M; r += RL_ORDER_THREADS) a.order[atomicAdd(&cnt[bin_of_row(r)], 1u)] = r;
 }
 
-template <bool VEC>
+// CAP: on-chip stash entries (a.rlcap <= CAP).  Short pitches take a smaller
+// stash, so that more workgroups share a CU: 78 KB of LDS at STASH_CAP (two
+// per CU), about 49 KB at 4096 entries (three), about 33 KB at 2048 (four).
+template <bool VEC, int CAP>
 __global__ __launch_bounds__(RL_THREADS, 4) void k_ragged_rowlocal(RaggedArgs a)
 {
-    __shared__ SelectSmem sm;
+    __shared__ SelectSmemT<CAP> sm;
     __shared__ BoundaryOut bq[2];  // primary, secondary boundary
     __shared__ float s_e[2];
     __shared__ uint32_t s_cnt;
@@ -521,7 +525,7 @@ __global__ __launch_bounds__(RL_THREADS, 4) void k_ragged_rowlocal(RaggedArgs a)
         return;
     }
     const float *row = a.scores + (size_t)r * (size_t)a.pitch;
-    const uint32_t cap = (uint32_t)a.rlcap;  // <= STASH_CAP
+    const uint32_t cap = (uint32_t)a.rlcap;  // <= CAP
 
     // Chunk c: lane-interleaved 16-byte pieces of the row's whole pieces
     // (the last 1-3 scores of a row whose length is not a multiple of 4 are
@@ -745,7 +749,9 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     // one workgroup, and a secondary count that leaves room in the on-chip
     // stash.  Tests pick a mapping with the ragged_route knob (a segment
     // count also selects the segmented route).
-    const int rlcap = kn.capacity > 0 && kn.capacity < STASH_CAP ? kn.capacity : STASH_CAP;
+    // Short pitches use a smaller stash (more workgroups per CU).
+    const int stash = pitch <= RL_TINY_CAP ? RL_TINY_CAP : pitch <= RL_SMALL_CAP ? RL_SMALL_CAP : STASH_CAP;
+    const int rlcap = kn.capacity > 0 && kn.capacity < stash ? kn.capacity : stash;
     // A pitch that fits the stash takes the row-local mapping at any row
     // count: one launch instead of two (rows of 1K-7.7K scores, 1 to 256
     // rows: 7-12 us against 13-17 us segmented).
@@ -754,6 +760,7 @@ RaggedPlan plan_ragged(int32_t M, int64_t pitch, int32_t k)
     if (rl_fits && (kn.route_select == 2 || kn.route_select == 3 ||
                     (kn.route_select == 0 && kn.splits == 0 && (M >= RAG_RL_MIN_ROWS || fits_chip)))) {
         p.rowlocal = true;
+        p.rlstash = stash;
         p.rlcap = rlcap;
         // Direct-exact rows: a row no longer than the sampled steps' expected
         // candidate count plus RAG_DIRECT_MARGIN is refined whole (the view's
@@ -835,14 +842,24 @@ hipError_t launch_ragged(const RaggedPlan &p, const float *scores, const int32_t
     if (p.rowlocal) {
         StageTimer st(ST_RAG_ROWLOCAL, stream);
         // Below RAG_RL_MIN_ROWS rows every workgroup is resident at once, so
-        // the order would change nothing: workgroup b takes row b.
-        if (p.M >= RAG_RL_MIN_ROWS) {
+        // the order would change nothing: workgroup b takes row b.  Nor is it
+        // launched when every row takes the direct steps: their times vary
+        // far less than those of sampled rows, and the order launch costs
+        // more than it saves (8192 rows of at most 2048 scores: 58 us
+        // without it, 67 us with it).
+        if (p.M >= RAG_RL_MIN_ROWS && p.pitch > (int64_t)p.direct_max) {
             a.order = reinterpret_cast<int32_t *>(w + p.off_order);
             e = launch_kernel(k_ragged_order, dim3(1), dim3(RL_ORDER_THREADS), stream, a);
             if (e != hipSuccess) return e;
         }
-        return vec ? launch_kernel(k_ragged_rowlocal<true>, dim3(p.M), dim3(RL_THREADS), stream, a)
-                   : launch_kernel(k_ragged_rowlocal<false>, dim3(p.M), dim3(RL_THREADS), stream, a);
+        if (p.rlstash == RL_TINY_CAP)
+            return vec ? launch_kernel(k_ragged_rowlocal<true, RL_TINY_CAP>, dim3(p.M), dim3(RL_THREADS), stream, a)
+                       : launch_kernel(k_ragged_rowlocal<false, RL_TINY_CAP>, dim3(p.M), dim3(RL_THREADS), stream, a);
+        if (p.rlstash == RL_SMALL_CAP)
+            return vec ? launch_kernel(k_ragged_rowlocal<true, RL_SMALL_CAP>, dim3(p.M), dim3(RL_THREADS), stream, a)
+                       : launch_kernel(k_ragged_rowlocal<false, RL_SMALL_CAP>, dim3(p.M), dim3(RL_THREADS), stream, a);
+        return vec ? launch_kernel(k_ragged_rowlocal<true, STASH_CAP>, dim3(p.M), dim3(RL_THREADS), stream, a)
+                   : launch_kernel(k_ragged_rowlocal<false, STASH_CAP>, dim3(p.M), dim3(RL_THREADS), stream, a);
     }
     {
         StageTimer st(ST_RAG_SCAN, stream);
