@@ -16,6 +16,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libitk.so")
+PROBE_LIB_PATH = os.path.join(HERE, "libitk_probe.so")
 
 F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
 FLAG_NO_RELU = 1
@@ -24,6 +25,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "
 RAGGED_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
+_probe_lib = None
 
 
 class ITKError(RuntimeError):
@@ -86,15 +88,28 @@ def lib():
         L.itk_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32),
                                        ctypes.POINTER(ctypes.c_char_p), I32]
         L.itk_profile_read.restype = I32
-        for name in ("itk_debug_mfma", "itk_debug_fp8", "itk_debug_coarse"):
+        _lib = L
+    return _lib
+
+
+def probe_lib():
+    """Load libitk_probe.so, the test-only probes of the device building
+    blocks (include/itk_probe.h); raise if it is missing."""
+    global _probe_lib
+    if _probe_lib is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise ImportError(f"{PROBE_LIB_PATH} is missing: run indexer_exact_top_amd/build.py (hipcc, gfx950)")
+        lib()  # torch and the HIP runtime first, as for the product library
+        L = ctypes.CDLL(PROBE_LIB_PATH)
+        P, I32 = ctypes.c_void_p, ctypes.c_int32
+        for name in ("itk_debug_mfma", "itk_debug_fp8", "itk_debug_coarse", "itk_debug_stream_read"):
             getattr(L, name).restype = ctypes.c_int
         L.itk_debug_mfma.argtypes = [I32, P, P, P, P]
         L.itk_debug_fp8.argtypes = [P, P, P, I32, P]
         L.itk_debug_coarse.argtypes = [P, P, P, I32, P]
-        L.itk_debug_stream_read.restype = ctypes.c_int
         L.itk_debug_stream_read.argtypes = [P, ctypes.c_uint64, P, I32, P]
-        _lib = L
-    return _lib
+        _probe_lib = L
+    return _probe_lib
 
 
 def require_gpu():
@@ -360,7 +375,7 @@ def debug_mfma(mtype: int, a_frags, b_frags, acc=None):
     (mtype 4: the FP8 MFMA onto the accumulator values ``acc`` [64, 16])."""
     import torch
     c = torch.empty((64, 16), dtype=torch.float32, device=a_frags.device) if acc is None else acc.clone()
-    _check(lib().itk_debug_mfma(mtype, _ptr(a_frags), _ptr(b_frags), _ptr(c), _stream(None)), "itk_debug_mfma")
+    _check(probe_lib().itk_debug_mfma(mtype, _ptr(a_frags), _ptr(b_frags), _ptr(c), _stream(None)), "itk_debug_mfma")
     return c
 
 
@@ -368,7 +383,7 @@ def debug_fp8(codes):
     import torch
     bf = torch.empty(codes.numel(), dtype=torch.int16, device=codes.device)
     hf = torch.empty(codes.numel(), dtype=torch.int16, device=codes.device)
-    _check(lib().itk_debug_fp8(_ptr(codes), _ptr(bf), _ptr(hf), codes.numel(), _stream(None)), "itk_debug_fp8")
+    _check(probe_lib().itk_debug_fp8(_ptr(codes), _ptr(bf), _ptr(hf), codes.numel(), _stream(None)), "itk_debug_fp8")
     return bf, hf
 
 
@@ -377,7 +392,7 @@ def debug_coarse(x):
     n = x.numel()
     key = torch.empty(n, dtype=torch.int32, device=x.device)
     ep = torch.empty(n, dtype=torch.float32, device=x.device)
-    _check(lib().itk_debug_coarse(_ptr(x), _ptr(key), _ptr(ep), n, _stream(None)), "itk_debug_coarse")
+    _check(probe_lib().itk_debug_coarse(_ptr(x), _ptr(key), _ptr(ep), n, _stream(None)), "itk_debug_coarse")
     return key, ep
 
 
@@ -386,6 +401,6 @@ def debug_stream_read(x, blocks: int = 2048, out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty(blocks, dtype=torch.float32, device=x.device)
-    _check(lib().itk_debug_stream_read(_ptr(x), x.numel() * x.element_size(), _ptr(out), blocks, _stream(stream)),
+    _check(probe_lib().itk_debug_stream_read(_ptr(x), x.numel() * x.element_size(), _ptr(out), blocks, _stream(stream)),
            "itk_debug_stream_read")
     return out

@@ -1,5 +1,9 @@
-// Test-only probes of the layouts and conversions the fused kernels rely on.
+// Test-only probes of the layouts and conversions the fused kernels rely on,
+// built into their own library (libitk_probe.so, declared in itk_probe.h) so
+// that the product library carries none of them.  They compile the product's
+// device building blocks from the same headers.
 #include "fused_impl.hpp"
+#include "itk_probe.h"
 
 namespace itk {
 

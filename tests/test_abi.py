@@ -11,8 +11,8 @@ import indexer_exact_top_amd as itk
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "itk.h")).read()
+def _declared_functions(header="itk.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)
     return sorted({n for n in names if n.startswith(("itk_", "topk_", "indexer_"))})
@@ -24,6 +24,19 @@ def test_every_declared_symbol_is_exported():
     assert "indexer_topk_fused" in names and "topk_ragged" in names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
+
+
+def test_probes_live_in_their_own_library():
+    """The test-only probes (itk_probe.h) are exported by libitk_probe.so
+    and not by the product library."""
+    names = _declared_functions("itk_probe.h")
+    assert names == ["itk_debug_coarse", "itk_debug_fp8", "itk_debug_mfma", "itk_debug_stream_read"]
+    probe = itk.probe_lib()
+    for n in names:
+        assert hasattr(probe, n), f"missing export {n}"
+    product = ctypes.CDLL(itk.LIB_PATH)
+    for n in names:
+        assert not hasattr(product, n), f"{n} exported by the product library"
 
 
 def test_status_strings():
