@@ -163,6 +163,26 @@ def test_plan_opts_validation():
     assert lib.itk_set_plan_opts(None) == 0
 
 
+def test_short_pitches_take_the_row_local_mapping_at_any_row_count():
+    """A pitch that fits the on-chip stash (7680 scores) takes the row-local
+    mapping however few rows there are; its only scratch is the row order
+    (4 B per row, 256-byte aligned), where the segmented mapping needs
+    per-segment candidate slices.  A longer pitch at few rows stays
+    segmented."""
+    lib = itk.lib()
+    assert lib.itk_set_plan_opts(None) == 0
+    for M in (1, 8, 64, 511):
+        for pitch, k in ((7680, 2048), (4096, 64), (2048, 100), (7679, 8000)):
+            assert lib.topk_ragged_workspace_size(M, pitch, k) == (4 * M + 255) // 256 * 256, (M, pitch, k)
+    assert lib.topk_ragged_workspace_size(64, 7681, 2048) > 64 * 2048
+    # the segments knob (route 1) keeps the segmented mapping for short pitches too
+    assert lib.itk_set_plan_opts(ctypes.byref(itk.PlanOpts(0, 0, 0, 0, 0, 0, 1))) == 0
+    try:
+        assert lib.topk_ragged_workspace_size(64, 4096, 64) > 64 * 64
+    finally:
+        assert lib.itk_set_plan_opts(None) == 0
+
+
 def test_history_sample_validation():
     lib = itk.lib()
     BF, F16 = itk.BF16, itk.F16
