@@ -341,6 +341,18 @@ def csa_chunk(S: int, chunk: int, *, m: int = 4, k: int = 2048, H: int = 64, D: 
                      seed=seed, name=f"csa_chunk_S{S}_m{m}")
 
 
+def long_context_chunk(T: int = 8192, N: int = 1 << 20, *, k: int = 2048, H: int = 64, D: int = 128,
+                       seed: int = 808) -> FusedCase:
+    """The last T query tokens of an N-token prefill (LiteTopK Sec. 4, the
+    kernel evaluation at 1M context, chunk 8192, k = 2048): bf16 Q, FP8 e4m3
+    keys with per-key scales, H indexer heads of dimension D, and causal
+    lengths kv_len[t] = N - T + 1 + t (each query sees the keys up to and
+    including its own token).  Values as in the other fused workloads."""
+    kv = np.arange(N - T + 1, N + 1, dtype=np.int64)
+    return gen_fused(T, H, D, N, k, q_dtype=BF16, k_dtype=FP8_E4M3, kv_len=kv.astype(np.int32), seed=seed,
+                     name=f"long_context_chunk_T{T}_N{N}")
+
+
 def prefill_chunk_pair(T, H, D, N, k, *, start: Optional[int] = None, n_hot: Optional[int] = None,
                        k_dtype=BF16, seed: int = 707, name: str = "prefill_chunk_pair"):
     """Two consecutive query chunks of one prefill over shared keys, with the
