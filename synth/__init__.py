@@ -343,8 +343,9 @@ def csa_chunk(S: int, chunk: int, *, m: int = 4, k: int = 2048, H: int = 64, D: 
 
 def long_context_chunk(T: int = 8192, N: int = 1 << 20, *, k: int = 2048, H: int = 64, D: int = 128,
                        seed: int = 808) -> FusedCase:
-    """The last T query tokens of an N-token prefill (LiteTopK Sec. 4, the
-    kernel evaluation at 1M context, chunk 8192, k = 2048): bf16 Q, FP8 e4m3
+    """The last T query tokens of an N-token prefill (the shape of LiteTopK
+    Sec. 4.1 "Sparse-Attention Kernel Benchmark" and Sec. 4.2, Fig. 5(a):
+    1M context, chunk 8192, k = 2048): bf16 Q, FP8 e4m3
     keys with per-key scales, H indexer heads of dimension D, and causal
     lengths kv_len[t] = N - T + 1 + t (each query sees the keys up to and
     including its own token).  Values as in the other fused workloads."""
